@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Throughput of the PISA block-sparse attention path on one MI355X.
+
+A step is one pass of the whole prefill path -- key pyramid, top-K selection,
+sparse attention -- over the 128K-token GQA workload (B=1, 32 query heads on 8
+KV heads, N=131072, d=128, bf16, block 128, fanout 8, 4 levels, K=32, 64-token
+sink, one local block). Inputs are synthetic (seeded), drawn on the GPU and
+resident in HBM before the timed region. Beside it the decode workload (64
+sequences x 131072-token cache, one new token each) is timed per step.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12  # B/s, MI355X
+BF16_PEAK = 2.5e15  # flop/s, dense bf16 matrix cores
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (what the method must move or compute; masked work excluded)
+
+
+def attended_pairs(p, idx, cnt):
+    """Sum over query rows of |attended keys| for a prefill (numpy, exact integers)."""
+    import numpy as np
+
+    bs, s, N, G = p.block_size, p.sink_len, p.seq_len, p.group
+    nb = p.n_blocks
+    j0 = s // bs
+    qb = np.arange(nb)
+    rows = np.minimum(bs, N - qb * bs).astype(np.int64)
+    s_eff = np.minimum(s, qb * bs)
+    total = 0
+    for b in range(cnt.shape[0]):
+        for g in range(cnt.shape[1]):
+            c = cnt[b, g].astype(np.int64)
+            first = idx[b, g, :, 0] if idx.shape[-1] else np.full(nb, -1)
+            has_j0 = (c > 0) & (first == j0)
+            overlap = np.where(has_j0 & (j0 * bs < s_eff), np.minimum(s_eff, (j0 + 1) * bs) - j0 * bs, 0)
+            before = c * bs + s_eff - overlap
+            total += int(np.sum(rows * before + rows * (rows + 1) // 2)) * G
+    return total
+
+
+def pyramid_bytes(p, nodes):
+    elt = 2 if p.dtype == "bf16" else 4
+    return p.batch * p.heads_kv * p.seq_len * p.head_dim * elt + p.batch * p.heads_kv * nodes * p.head_dim * 4
+
+
+def select_bytes(p, nodes):
+    elt = 2 if p.dtype == "bf16" else 4
+    nb = p.n_blocks
+    return (p.batch * p.heads_q * p.seq_len * p.head_dim * elt + p.batch * p.heads_kv * nodes * p.head_dim * 4 +
+            p.batch * p.heads_kv * nb * (p.top_k + 1) * 4)
+
+
+def decode_scored_nodes(p, cache_len):
+    """Pool sizes of the descent for the decode token (no sink filtering needed at these shapes)."""
+    f, L, K, bs = p.fanout, p.levels, p.top_k, p.block_size
+    qb = (cache_len - 1) // bs
+    j0 = p.sink_len // bs
+    span = [f ** l for l in range(L)]
+    anc = [qb // s for s in span]
+    pool = max(0, anc[L - 1] - j0 // span[L - 1])
+    total = pool
+    for l in range(L - 1, 0, -1):
+        kept = min(K, pool)
+        pool = kept * f + (anc[l - 1] - anc[l] * f)
+        total += pool
+    return total
+
+
+def decode_bytes(p, cache_len, cnt):
+    """K/V rows attended + pyramid rows scored + q + out, for one step."""
+    bs, s, d = p.block_size, p.sink_len, p.head_dim
+    pos = cache_len - 1
+    qb = pos // bs
+    total_keys = 0
+    for b in range(cnt.shape[0]):
+        for g in range(cnt.shape[1]):
+            c = int(cnt[b, g])
+            total_keys += c * bs + min(s, qb * bs) + (pos - qb * bs + 1)  # sink overlap with block 0 ignored
+    kv = total_keys * d * 2 * 2
+    summaries = p.batch * p.heads_kv * decode_scored_nodes(p, cache_len) * d * 4
+    qo = 2 * p.batch * p.heads_q * d * 2
+    return kv + summaries + qo
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle on a bounded sample
+
+
+def cpu_baseline(p, q, k, v, seed_units=0):
+    """Time the oracle (numpy fp64) on a sample of the prefill workload and scale to tokens/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t_all = time.perf_counter()
+    G, bs, nb = p.group, p.block_size, p.n_blocks
+    # the oracle sees one KV head at a time: Q of its group, its K and V
+    n_heads = 2
+    qh = [q[:, g * G:(g + 1) * G].float().cpu().numpy() for g in range(n_heads)]
+    kh = [k[:, g:g + 1].float().cpu().numpy() for g in range(n_heads)]
+    vh = [v[:, g:g + 1].float().cpu().numpy() for g in range(n_heads)]
+    # stage 1: pyramid of n_heads KV heads (full length)
+    t0 = time.perf_counter()
+    pyr = [oracle.build_pyramid(kk, bs, p.fanout, p.levels) for kk in kh]
+    t_pyr = (time.perf_counter() - t0) / n_heads * p.heads_kv
+    # stage 2: selection of a sample of query blocks
+    t0 = time.perf_counter()
+    qbar = [oracle.query_block_means(qq, 1, bs) for qq in qh]
+    t_qbar = (time.perf_counter() - t0) / n_heads * p.heads_kv
+    rng = np.random.default_rng(seed_units)
+    sel_units = np.sort(rng.choice(nb, 384, replace=False))
+    sels = {}
+    t0 = time.perf_counter()
+    for qb in sel_units:
+        lv = [lvl[0, 0] for lvl in pyr[0]]
+        sels[int(qb)] = oracle.descend(lv, qbar[0][0, 0, qb], int(qb), p.top_k, p.sink_len, bs, p.fanout)
+    t_sel = (time.perf_counter() - t0) / len(sel_units) * nb * p.heads_kv + t_qbar
+    # stage 3: attention for a sample of units (all G heads, all rows)
+    att_units = sel_units[::8]
+    t0 = time.perf_counter()
+    for qb in att_units:
+        sel = sels[int(qb)]
+        r0, r1 = int(qb) * bs, min(p.seq_len, (int(qb) + 1) * bs)
+        for h in range(G):
+            oracle.attend_block(qh[0][0, h, r0:r1], kh[0][0, 0], vh[0][0, 0], r0, sel, p.sink_len, bs, p.scale)
+    t_att = (time.perf_counter() - t0) / len(att_units) * nb * p.heads_kv
+    total = t_pyr + t_sel + t_att
+    return dict(
+        value=p.batch * p.seq_len / total,
+        unit="tokens/s",
+        cores=int(threads),
+        kind="oracle",
+        sample=(f"pyramid of {n_heads}/{p.heads_kv} KV heads (full length), selection of {len(sel_units)} query "
+                f"blocks and attention of {len(att_units)} query blocks x {G} heads of KV head 0, each stage scaled "
+                f"to all {nb * p.heads_kv} units; stage seconds extrapolated: pyramid {t_pyr:.1f}, selection "
+                f"{t_sel:.1f}, attention {t_att:.1f}; sample wall time {time.perf_counter() - t_all:.1f} s"),
+    )
+
+
+# ---------------------------------------------------------------------------
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no multi-GPU path", flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_sparse_long_pisa_amd as pisa
+    import gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = gen.config(3)
+    p = cfg["problem"]
+    cp = pisa.problem(p.batch, p.heads_q, p.heads_kv, p.seq_len, p.head_dim, p.block_size, p.fanout, p.levels,
+                      p.top_k, p.sink_len, p.dtype)
+    log(f"generating {cfg['name']} on the GPU")
+    q, k, v, _ = gen.device_inputs(p, cfg["seed"], cfg["value_scale"], cfg["plant"], device=dev)
+    nodes = pisa.pyramid_layout(cp)[-1]
+    nb = p.n_blocks
+    pyr = torch.empty((p.batch, p.heads_kv, nodes, p.head_dim), dtype=torch.float32, device=dev)
+    idx = torch.empty((p.batch, p.heads_kv, nb, p.top_k), dtype=torch.int32, device=dev)
+    cnt = torch.empty((p.batch, p.heads_kv, nb), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        pisa.build_pyramid(cp, k, pyr)
+        if ev is not None:
+            ev[1].record()
+        pisa.select_topk(cp, q, pyr, idx, cnt)
+        if ev is not None:
+            ev[2].record()
+        pisa.sparse_attn_fwd(cp, q, k, v, idx, cnt, out)
+        if ev is not None:
+            ev[3].record()
+
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    # per-kernel durations with HIP events on the launch stream (torch's current stream)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    t_pool = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    t_sel = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    t_att = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e-3
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    pairs = attended_pairs(p, idx_h, cnt_h)
+    flops = 4.0 * p.head_dim * pairs
+    b_pool = pyramid_bytes(p, nodes)
+    b_sel = select_bytes(p, nodes)
+    log(f"prefill {ms_per_step:.3f} ms/step: pyramid {t_pool * 1e3:.3f} ms, select {t_sel * 1e3:.3f} ms, "
+        f"attention {t_att * 1e3:.3f} ms ({flops / t_att / 1e12:.1f} TFLOP/s)")
+
+    result = {
+        "metric": "sparse-attn prefill tokens/s @128K + decode µs/step; % HBM & MFMA peak",
+        "value": p.batch * p.seq_len / (elapsed / args.steps),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "PISA prefill, bf16 causal GQA 32q/8kv heads, N=131072, d=128, block 128, fanout 8, "
+                        "4 levels, K=32, 64-token sink, 1 local block; planted needles at 16 depths per KV head",
+            "batch": p.batch, "seq_len": p.seq_len, "heads_q": p.heads_q, "heads_kv": p.heads_kv,
+            "head_dim": p.head_dim, "block_size": p.block_size, "fanout": p.fanout, "levels": p.levels,
+            "top_k": p.top_k, "sink_len": p.sink_len, "seed": cfg["seed"],
+        },
+        "roofline": {
+            "kernel": "attn_bf16_kernel (sparse attention)",
+            "bound": "mfma",
+            "achieved": flops / t_att / 1e12,
+            "peak": BF16_PEAK / 1e12,
+            "unit": "TFLOP/s",
+            "frac": flops / t_att / BF16_PEAK,
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops,
+            "avg_launch_ms": t_att * 1e3,
+        },
+        "kernels": {
+            "pyramid": {"ms": t_pool * 1e3, "bound": "hbm", "bytes": b_pool, "GB/s": b_pool / t_pool / 1e9,
+                        "frac": b_pool / t_pool / HBM_PEAK},
+            "select": {"ms": t_sel * 1e3, "bound": "hbm", "bytes": b_sel, "GB/s": b_sel / t_sel / 1e9,
+                       "frac": b_sel / t_sel / HBM_PEAK},
+            "attention": {"ms": t_att * 1e3, "bound": "mfma", "flops": flops, "TFLOP/s": flops / t_att / 1e12,
+                          "frac": flops / t_att / BF16_PEAK, "attended_pairs": pairs},
+        },
+    }
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
+        bcopy = torch.empty_like(a)
+        torch.cuda.synchronize()
+        bcopy.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = 2 * a.numel() * 2
+        del a, bcopy
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(p, q, k, v)
+    del q, k, v, out, pyr
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        dcfg = gen.config(4)
+        dp = dcfg["problem"]
+        dcp = pisa.problem(dp.batch, dp.heads_q, dp.heads_kv, dp.seq_len, dp.head_dim, dp.block_size, dp.fanout,
+                           dp.levels, dp.top_k, dp.sink_len, dp.dtype)
+        cache_len = dp.seq_len
+        log(f"generating {dcfg['name']} on the GPU")
+        dq, kc, vc, _ = gen.device_decode_inputs(dp, dcfg["seed"], dcfg["value_scale"], cache_len, device=dev)
+        dpyr = pisa.build_pyramid(dcp, kc)  # built once over the cache, not timed
+        ws = torch.empty(pisa.decode_workspace_size(dcp), dtype=torch.uint8, device=dev)
+        dout = torch.empty_like(dq)
+        didx = torch.empty((dp.batch, dp.heads_kv, dp.top_k), dtype=torch.int32, device=dev)
+        dcnt = torch.empty((dp.batch, dp.heads_kv), dtype=torch.int32, device=dev)
+        for _ in range(args.warmup):
+            pisa.decode_step(dcp, dq, kc, vc, dpyr, cache_len, out=dout, idx_out=didx, cnt_out=dcnt, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(args.decode_steps):
+            pisa.decode_step(dcp, dq, kc, vc, dpyr, cache_len, out=dout, idx_out=didx, cnt_out=dcnt, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        t_dec = (time.perf_counter() - t0) / args.decode_steps
+        t_dec_ev = e0.elapsed_time(e1) * 1e-3 / args.decode_steps
+        db = decode_bytes(dp, cache_len, dcnt.cpu().numpy())
+        log(f"decode {t_dec * 1e6:.1f} us/step ({db / t_dec_ev / 1e9:.0f} GB/s)")
+        result["decode"] = {
+            "workload": "PISA decode, bf16 GQA 32q/8kv, 64 sequences x 131072-token cache, one new token each, "
+                        "block 128, fanout 8, 4 levels, K=32, 64-token sink",
+            "us_per_step": t_dec * 1e6,
+            "us_per_step_events": t_dec_ev * 1e6,
+            "tokens_per_s": dp.batch / t_dec,
+            "steps": args.decode_steps,
+            "bound": "hbm",
+            "bytes_per_step": db,
+            "GB/s": db / t_dec_ev / 1e9,
+            "frac": db / t_dec_ev / HBM_PEAK,
+        }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,326 @@
+// One decode step: a new query token per sequence, its key and value already in
+// the cache. Selection reuses the pyramid descent of "La sélection top-K guidée
+// par la pyramide" with a one-token query block; attention over the attended
+// blocks is split across workgroups and the partial results are merged with an
+// online softmax, as the Pulsar Attention page merges per-host partial
+// attentions ("Phase 2 : Encodage de la requête globale").
+//
+// Three launches on the caller's stream:
+//   decode_select  one workgroup per (batch, kv head): fp64 mean of the group's
+//                  query rows, descent, block list into the workspace;
+//   decode_attn    (split, batch, kv head): streams its share of the K rows,
+//                  keeps all its logits in LDS, then streams the V rows once;
+//                  writes (max, sum, unnormalised output) per query head;
+//   decode_merge   one workgroup per (batch, query head): merges the splits.
+// The step is bound by HBM: it reads each attended K/V row exactly once.
+#include "pisa_internal.h"
+#include "pisa_select_common.h"
+
+namespace pisa {
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kTilesPerSplit = 4;
+constexpr int kMaxGroup = 8;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct DecodeWs {
+  int32_t* idx;  // [B*Hkv, K]
+  int32_t* cnt;  // [B*Hkv]
+  float* m;      // [B*Hkv, S, G]  log2-domain max
+  float* l;      // [B*Hkv, S, G]
+  float* o;      // [B*Hkv, S, G, D] unnormalised
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(Geo g, const T* __restrict__ q,
+                                                                       const float* __restrict__ pyr, int qb,
+                                                                       int32_t* __restrict__ idx,
+                                                                       int32_t* __restrict__ cnt) {
+  __shared__ double qbar[D];
+  __shared__ DescentSmem sm;
+  const int slab = blockIdx.x;
+  const int b = slab / g.Hkv;
+  const int kvh = slab % g.Hkv;
+  for (int c = threadIdx.x; c < D; c += kSelectThreads) {
+    double s = 0.0;
+    for (int hh = 0; hh < g.G; ++hh) {
+      const T* row = q + ((int64_t)b * g.Hq + kvh * g.G + hh) * D;
+      float x;
+      if constexpr (sizeof(T) == 2) x = bf16_to_f32(((const uint16_t*)row)[c]);
+      else x = ((const float*)row)[c];
+      s += (double)x;
+    }
+    qbar[c] = s / (double)g.G;
+  }
+  __syncthreads();
+  descend<D>(g, pyr + (int64_t)slab * g.off[g.L] * D, qbar, qb, idx + (int64_t)slab * g.K, cnt + slab, sm);
+}
+
+// Block walk of the decode token (position pos, block qb): full sink blocks,
+// partial sink block, selected blocks, local block [qb*bs, pos].
+__device__ __forceinline__ void decode_tile(const Geo& g, int qb, int pos, const int* sel, int nsel, int t, int& j,
+                                            int& nvalid) {
+  const int nfull = min(g.j0, qb);
+  const bool tail = g.sink > g.j0 * g.bs && g.j0 < qb && !(nsel > 0 && sel[0] == g.j0);
+  const int np = tail ? 1 : 0;
+  if (t < nfull) {
+    j = t;
+    nvalid = g.bs;
+  } else if (t < nfull + np) {
+    j = g.j0;
+    nvalid = g.sink - g.j0 * g.bs;
+  } else if (t < nfull + np + nsel) {
+    j = sel[t - nfull - np];
+    nvalid = g.bs;
+  } else {
+    j = qb;
+    nvalid = pos - qb * g.bs + 1;
+  }
+}
+
+__device__ __forceinline__ int decode_ntiles(const Geo& g, int qb, const int* sel, int nsel) {
+  const bool tail = g.sink > g.j0 * g.bs && g.j0 < qb && !(nsel > 0 && sel[0] == g.j0);
+  return min(g.j0, qb) + (tail ? 1 : 0) + nsel + 1;
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T* __restrict__ q,
+                                                                  const T* __restrict__ kc, const T* __restrict__ vc,
+                                                                  int qb, int pos, int splits, DecodeWs ws) {
+  constexpr int VEC = Wide<T>::kVec;
+  constexpr int LPR = D / VEC;                // lanes per cache row
+  constexpr int RP = kDecThreads / LPR;       // rows per pass of the workgroup
+  constexpr int MAXK = kTilesPerSplit * 128;  // keys per split (bs <= 128)
+  __shared__ float qs[G][D];
+  __shared__ float sc[MAXK][G];  // logits (log2 domain) of this split's keys
+  __shared__ int sel[kMaxTopK];
+  __shared__ float red[kDecThreads / 64][G][D];
+  __shared__ float mred[G];
+
+  const int split = blockIdx.x;
+  const int slab = blockIdx.y;
+  const int b = slab / g.Hkv;
+  const int kvh = slab % g.Hkv;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = (tid % LPR) * VEC;
+  const int rsub = tid / LPR;
+  const int nsel = ws.cnt[slab];
+  for (int t = tid; t < nsel; t += kDecThreads) sel[t] = ws.idx[(int64_t)slab * g.K + t];
+  for (int e = tid; e < G * D; e += kDecThreads) {
+    const T* row = q + ((int64_t)b * g.Hq + kvh * G + e / D) * D;
+    float x;
+    if constexpr (sizeof(T) == 2) x = bf16_to_f32(((const uint16_t*)row)[e % D]);
+    else x = ((const float*)row)[e % D];
+    qs[e / D][e % D] = x;
+  }
+  __syncthreads();
+  float qr[G][VEC];  // this lane's column slice of every head's query
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) qr[hh][e] = qs[hh][col + e];
+  const int ntiles = decode_ntiles(g, qb, sel, nsel);
+  const int t0 = split * kTilesPerSplit;
+  const int t1 = min(ntiles, t0 + kTilesPerSplit);
+  const T* kb = kc + (int64_t)slab * g.N * D;
+  const T* vb = vc + (int64_t)slab * g.N * D;
+  const float c = g.scale * kLog2e;
+
+  // pass 1: logits of every key of this split
+  int nkeys = 0;
+  for (int t = t0; t < t1; ++t) {
+    int j, nvalid;
+    decode_tile(g, qb, pos, sel, nsel, t, j, nvalid);
+    for (int r = rsub; r < g.bs; r += RP) {
+      float x[VEC];
+      const bool in = r < nvalid;
+      if (in) Wide<T>::load(kb + ((int64_t)j * g.bs + r) * D + col, x);
+      float part[G];
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float s = 0.f;
+        if (in) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) s = fmaf(qr[hh][e], x[e], s);
+        }
+        part[hh] = s;
+      }
+#pragma unroll
+      for (int sh = 1; sh < LPR; sh <<= 1)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) part[hh] += __shfl_xor(part[hh], sh);
+      if ((tid % LPR) == 0) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) sc[nkeys + r][hh] = in ? part[hh] * c : -__builtin_inff();
+      }
+    }
+    nkeys += g.bs;
+  }
+  __syncthreads();
+  // per-head max over the split
+  if (tid < G) {
+    float mx = -__builtin_inff();
+    for (int r = 0; r < nkeys; ++r) mx = fmaxf(mx, sc[r][tid]);
+    mred[tid] = mx;
+  }
+  __syncthreads();
+  float mh[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) mh[hh] = mred[hh] == -__builtin_inff() ? 0.f : mred[hh];
+  // pass 2: stream V once, weights exp2(logit - max)
+  float acc[G][VEC];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[hh][e] = 0.f;
+  int base = 0;
+  for (int t = t0; t < t1; ++t) {
+    int j, nvalid;
+    decode_tile(g, qb, pos, sel, nsel, t, j, nvalid);
+    for (int r = rsub; r < nvalid; r += RP) {
+      float x[VEC];
+      Wide<T>::load(vb + ((int64_t)j * g.bs + r) * D + col, x);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        const float p = exp2f(sc[base + r][hh] - mh[hh]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[hh][e] = fmaf(p, x[e], acc[hh][e]);
+      }
+    }
+    base += g.bs;
+  }
+  // sum the row slots: within the wave by shuffles, across waves in LDS
+#pragma unroll
+  for (int sh = LPR; sh < 64; sh <<= 1)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[hh][e] += __shfl_xor(acc[hh][e], sh);
+  if (lane < LPR) {
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) red[wave][hh][col + e] = acc[hh][e];
+  }
+  __syncthreads();
+  const int64_t pbase = ((int64_t)slab * splits + split) * G;
+  for (int e = tid; e < G * D; e += kDecThreads) {
+    const int hh = e / D, d = e % D;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecThreads / 64; ++w) s += red[w][hh][d];
+    ws.o[(pbase + hh) * D + d] = s;
+  }
+  if (tid < G) {
+    float l = 0.f;
+    for (int r = 0; r < nkeys; ++r) l += exp2f(sc[r][tid] - mh[tid]);
+    ws.m[pbase + tid] = mred[tid];
+    ws.l[pbase + tid] = l;
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(Geo g, int splits, DecodeWs ws, T* __restrict__ out,
+                                                         float* __restrict__ lse) {
+  const int bh = blockIdx.x;  // b * Hq + h
+  const int b = bh / g.Hq;
+  const int h = bh % g.Hq;
+  const int slab = b * g.Hkv + h / g.G;
+  const int hh = h % g.G;
+  float mstar = -__builtin_inff();
+  for (int s = 0; s < splits; ++s) mstar = fmaxf(mstar, ws.m[((int64_t)slab * splits + s) * g.G + hh]);
+  float l = 0.f, o = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const int64_t p = ((int64_t)slab * splits + s) * g.G + hh;
+    const float m = ws.m[p];
+    const float w = m == -__builtin_inff() ? 0.f : exp2f(m - mstar);
+    l += w * ws.l[p];
+    o += w * ws.o[p * D + threadIdx.x];
+  }
+  const float val = o / l;
+  if constexpr (sizeof(T) == 2) ((uint16_t*)out)[(int64_t)bh * D + threadIdx.x] = (uint16_t)f32_to_bf16(val);
+  else ((float*)out)[(int64_t)bh * D + threadIdx.x] = val;
+  if (lse != nullptr && threadIdx.x == 0) lse[bh] = (mstar + log2f(l)) * kLn2;
+}
+
+DecodeWs carve(const Geo& g, void* base, int splits) {
+  char* p = (char*)base;
+  auto take = [&](size_t bytes) {
+    char* r = p;
+    p += (bytes + 255) & ~(size_t)255;
+    return r;
+  };
+  const int64_t slabs = (int64_t)g.B * g.Hkv;
+  DecodeWs w;
+  w.idx = (int32_t*)take(sizeof(int32_t) * slabs * (g.K > 0 ? g.K : 1));
+  w.cnt = (int32_t*)take(sizeof(int32_t) * slabs);
+  w.m = (float*)take(sizeof(float) * slabs * splits * g.G);
+  w.l = (float*)take(sizeof(float) * slabs * splits * g.G);
+  w.o = (float*)take(sizeof(float) * slabs * splits * g.G * g.D);
+  return w;
+}
+
+}  // namespace
+
+// Worst-case block count of the walk: sink blocks, selected blocks, local block.
+int decode_splits(const Geo& g, int /*cache_len*/) {
+  const int sink_blocks = (g.sink + g.bs - 1) / g.bs;
+  const int tiles = min(g.nb, sink_blocks + g.K + 1);
+  return (tiles + kTilesPerSplit - 1) / kTilesPerSplit;
+}
+
+size_t decode_workspace_bytes(const Geo& g) {
+  const int splits = decode_splits(g, g.N);
+  const size_t slabs = (size_t)g.B * g.Hkv;
+  auto r = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  return r(sizeof(int32_t) * slabs * (g.K > 0 ? g.K : 1)) + r(sizeof(int32_t) * slabs) +
+         2 * r(sizeof(float) * slabs * splits * g.G) + r(sizeof(float) * slabs * splits * g.G * g.D);
+}
+
+template <typename T, int D>
+static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr,
+                                  int cache_len, void* out, float* lse, int32_t* idx_out, int32_t* cnt_out, void* wsb,
+                                  hipStream_t s) {
+  const int splits = decode_splits(g, cache_len);
+  DecodeWs ws = carve(g, wsb, splits);
+  const int slabs = g.B * g.Hkv;
+  const int pos = cache_len - 1;
+  const int qb = pos / g.bs;
+  hipLaunchKernelGGL((decode_select_kernel<T, D>), dim3(slabs), dim3(kSelectThreads), 0, s, g, (const T*)q, pyr, qb,
+                     ws.idx, ws.cnt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid(splits, slabs);
+  switch (g.G) {
+    case 1: hipLaunchKernelGGL((decode_attn_kernel<T, D, 1>), grid, dim3(kDecThreads), 0, s, g, (const T*)q, (const T*)kc, (const T*)vc, qb, pos, splits, ws); break;
+    case 2: hipLaunchKernelGGL((decode_attn_kernel<T, D, 2>), grid, dim3(kDecThreads), 0, s, g, (const T*)q, (const T*)kc, (const T*)vc, qb, pos, splits, ws); break;
+    case 4: hipLaunchKernelGGL((decode_attn_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, s, g, (const T*)q, (const T*)kc, (const T*)vc, qb, pos, splits, ws); break;
+    default: hipLaunchKernelGGL((decode_attn_kernel<T, D, 8>), grid, dim3(kDecThreads), 0, s, g, (const T*)q, (const T*)kc, (const T*)vc, qb, pos, splits, ws); break;
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(g.B * g.Hq), dim3(D), 0, s, g, splits, ws, (T*)out, lse);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (idx_out != nullptr && g.K > 0) {
+    e = hipMemcpyAsync(idx_out, ws.idx, sizeof(int32_t) * slabs * g.K, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+  }
+  if (cnt_out != nullptr) e = hipMemcpyAsync(cnt_out, ws.cnt, sizeof(int32_t) * slabs, hipMemcpyDeviceToDevice, s);
+  return e;
+}
+
+hipError_t launch_decode(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr, int cache_len,
+                         void* out, float* lse, int32_t* idx, int32_t* cnt, void* ws, hipStream_t s) {
+  if (g.dtype == PISA_BF16)
+    return g.D == 128 ? launch_decode_d<uint16_t, 128>(g, q, kc, vc, pyr, cache_len, out, lse, idx, cnt, ws, s)
+                      : launch_decode_d<uint16_t, 64>(g, q, kc, vc, pyr, cache_len, out, lse, idx, cnt, ws, s);
+  return g.D == 128 ? launch_decode_d<float, 128>(g, q, kc, vc, pyr, cache_len, out, lse, idx, cnt, ws, s)
+                    : launch_decode_d<float, 64>(g, q, kc, vc, pyr, cache_len, out, lse, idx, cnt, ws, s);
+}
+
+}  // namespace pisa

@@ -1,0 +1,84 @@
+// Internal declarations of the PISA HIP library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pisa.h"
+
+namespace pisa {
+
+constexpr int kMaxLevels = 8;
+constexpr int kPoolMax = 1024;  // largest candidate pool scored at one level
+constexpr int kMaxTopK = 256;
+
+// Problem geometry derived on the host from pisa_problem and passed to every
+// kernel by value. Node counts and offsets are per (batch, kv head) slab.
+struct Geo {
+  int B, Hq, Hkv, G, D;
+  int N;        // tokens (prefill) or cache capacity (decode)
+  int bs, nb;   // block size and number of (possibly partial) blocks
+  int f, L, K;  // fanout, levels, top-k
+  int sink, j0; // sink tokens; blocks wholly inside the sink
+  int dtype;
+  int nodes[kMaxLevels];
+  int off[kMaxLevels + 1];  // off[L] = nodes per slab
+  int span[kMaxLevels];     // blocks under one node of level l (f^l)
+  float scale;              // softmax scale
+};
+
+// ---------------------------------------------------------------------------
+// bf16 helpers (bf16 is carried as raw uint16 bits)
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (inputs here are finite)
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Load 16 bytes and widen to fp32: 8 values for bf16, 4 for fp32.
+template <typename T>
+struct Wide;
+template <>
+struct Wide<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ __forceinline__ static void load(const uint16_t* p, float* out) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    out[0] = bf16lo(u.x); out[1] = bf16hi(u.x);
+    out[2] = bf16lo(u.y); out[3] = bf16hi(u.y);
+    out[4] = bf16lo(u.z); out[5] = bf16hi(u.z);
+    out[6] = bf16lo(u.w); out[7] = bf16hi(u.w);
+  }
+};
+template <>
+struct Wide<float> {
+  static constexpr int kVec = 4;
+  __device__ __forceinline__ static void load(const float* p, float* out) {
+    float4 u = *reinterpret_cast<const float4*>(p);
+    out[0] = u.x; out[1] = u.y; out[2] = u.z; out[3] = u.w;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// launchers (each lives beside its kernels)
+
+hipError_t launch_build_pyramid(const Geo& g, const void* k, float* pyr, hipStream_t s);
+hipError_t launch_select(const Geo& g, const void* q, const float* pyr, int32_t* idx, int32_t* cnt, hipStream_t s);
+hipError_t launch_attn(const Geo& g, const void* q, const void* k, const void* v, const int32_t* idx,
+                       const int32_t* cnt, void* out, float* lse, hipStream_t s);
+
+// decode: selection of one token per (batch, kv head), split attention, merge
+int decode_splits(const Geo& g, int cache_len);
+size_t decode_workspace_bytes(const Geo& g);
+hipError_t launch_decode(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr, int cache_len,
+                         void* out, float* lse, int32_t* idx, int32_t* cnt, void* ws, hipStream_t s);
+
+}  // namespace pisa

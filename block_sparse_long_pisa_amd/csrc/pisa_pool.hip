@@ -1,0 +1,129 @@
+// Key pyramid by mean pooling ("Attention clairsemée PISA : noyaux Triton sans
+// matrice de scores", sections "Une pyramide de clés plutôt qu'un tapis
+// uniforme" and "Le pooling comme première réduction").
+//
+// Level 0 (one summary per key block) and level 1 come from one streaming pass
+// over K: a workgroup owns one level-1 node (fanout consecutive blocks), each
+// wave reduces whole blocks with 16-byte loads and fp64 accumulators, and the
+// workgroup folds its blocks' stored fp32 summaries into the level-1 node.
+// Coarser levels are tiny and fold from the level below in one launch each.
+#include "pisa_internal.h"
+
+namespace pisa {
+namespace {
+
+constexpr int kPoolThreads = 256;
+constexpr int kUnroll = 8;
+constexpr int kMaxChunk = 16;  // blocks per workgroup (fanout <= 16)
+
+template <typename T, int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_leaf_kernel(Geo g, const T* __restrict__ k,
+                                                                  float* __restrict__ pyr, int chunk_blocks) {
+  constexpr int VEC = Wide<T>::kVec;
+  constexpr int LPR = D / VEC;   // lanes covering one key row
+  constexpr int RPI = 64 / LPR;  // rows one wave instruction covers
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = (lane % LPR) * VEC;
+  const int rsub = lane / LPR;
+  const int slab = blockIdx.y;
+  const T* kb = k + (int64_t)slab * g.N * D;
+  float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
+
+  __shared__ float leaf[kMaxChunk][D];
+  const int j_first = blockIdx.x * chunk_blocks;
+  const int nblk = min(chunk_blocks, g.nb - j_first);
+
+  for (int jj = wave; jj < nblk; jj += kPoolThreads / 64) {
+    const int j = j_first + jj;
+    const int r0 = j * g.bs;
+    const int r1 = min(g.N, r0 + g.bs);
+    double acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+    for (int r = r0 + rsub; r < r1; r += RPI * kUnroll) {
+      float x[kUnroll][VEC];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int row = r + u * RPI;
+        if (row < r1) {
+          Wide<T>::load(kb + (int64_t)row * D + col, x[u]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x[u][e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += (double)x[u][e];
+    }
+    // sum the row slots that share these columns
+#pragma unroll
+    for (int s = LPR; s < 64; s <<= 1)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], s);
+    if (rsub == 0) {
+      const double inv_cnt = 1.0 / (double)(r1 - r0);
+      float outv[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        // bs is a power of two, so the multiply is exact for full blocks; a
+        // partial last block divides by its row count
+        const double mean = ((r1 - r0) == g.bs) ? acc[e] * inv_cnt : acc[e] / (double)(r1 - r0);
+        outv[e] = (float)mean;
+        leaf[jj][col + e] = outv[e];
+      }
+      float* dst = pb + (int64_t)j * D + col;
+#pragma unroll
+      for (int e = 0; e < VEC; e += 4) *reinterpret_cast<float4*>(dst + e) = make_float4(outv[e], outv[e + 1], outv[e + 2], outv[e + 3]);
+    }
+  }
+  if (g.L < 2) return;
+  __syncthreads();
+  for (int c = threadIdx.x; c < D; c += kPoolThreads) {
+    double s = 0.0;
+    for (int jj = 0; jj < nblk; ++jj) s += (double)leaf[jj][c];
+    pb[(int64_t)(g.off[1] + blockIdx.x) * D + c] = (float)(s / (double)nblk);
+  }
+}
+
+// One coarse level: node n of level l = mean of its children at level l - 1.
+template <int D>
+__global__ __launch_bounds__(D) void pool_coarse_kernel(Geo g, float* __restrict__ pyr, int l) {
+  const int n = blockIdx.x;
+  const int slab = blockIdx.y;
+  float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
+  const int c0 = n * g.f;
+  const int c1 = min(c0 + g.f, g.nodes[l - 1]);
+  double s = 0.0;
+  for (int c = c0; c < c1; ++c) s += (double)pb[(int64_t)(g.off[l - 1] + c) * D + threadIdx.x];
+  pb[(int64_t)(g.off[l] + n) * D + threadIdx.x] = (float)(s / (double)(c1 - c0));
+}
+
+template <typename T, int D>
+hipError_t launch_pool_t(const Geo& g, const void* k, float* pyr, hipStream_t s) {
+  const int slabs = g.B * g.Hkv;
+  const int chunk = g.L >= 2 ? g.f : 8;
+  dim3 grid((g.nb + chunk - 1) / chunk, slabs);
+  hipLaunchKernelGGL((pool_leaf_kernel<T, D>), grid, dim3(kPoolThreads), 0, s, g, (const T*)k, pyr, chunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int l = 2; l < g.L; ++l) {
+    hipLaunchKernelGGL((pool_coarse_kernel<D>), dim3(g.nodes[l], slabs), dim3(D), 0, s, g, pyr, l);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_build_pyramid(const Geo& g, const void* k, float* pyr, hipStream_t s) {
+  if (g.dtype == PISA_BF16) {
+    return g.D == 128 ? launch_pool_t<uint16_t, 128>(g, k, pyr, s) : launch_pool_t<uint16_t, 64>(g, k, pyr, s);
+  }
+  return g.D == 128 ? launch_pool_t<float, 128>(g, k, pyr, s) : launch_pool_t<float, 64>(g, k, pyr, s);
+}
+
+}  // namespace pisa

@@ -9,7 +9,9 @@ Workload recipe (the pages print no dataset that fits one GPU; these stand in
 for the long-context needle-retrieval workloads the Pulsar and SSA pages
 evaluate on):
 
-* Q, K, V are i.i.d. N(0, 1), scaled by 1/sqrt(d) for the bf16 workloads.
+* Q, K, V are i.i.d. N(0, 1), scaled by 1/sqrt(d) for the bf16 workloads
+  (a "sharp" test variant leaves Q and K unscaled, so logits have unit
+  spread, and keeps V at 1/sqrt(d)).
   Values are drawn in fp64, rounded to fp32, then (bf16 workloads) rounded to
   bf16 with round-to-nearest-even.
 * A planted block (a "needle") for query block qb of KV group g overwrites
@@ -158,6 +160,13 @@ def _to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
     return round_to_bf16(x) if dtype == "bf16" else x
 
 
+def _scales(value_scale):
+    """One scale for Q, K and V, or a (q, k, v) triple."""
+    if isinstance(value_scale, (tuple, list)):
+        return tuple(float(x) for x in value_scale)
+    return (float(value_scale),) * 3
+
+
 def _rng(seed: int, *keys: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, *keys])))
 
@@ -233,15 +242,16 @@ def host_inputs(p: Problem, seed: int, value_scale: float, plant=None):
     Returns (q, k, v, manifest).
     """
     B, Hq, Hkv, N, d = p.batch, p.heads_q, p.heads_kv, p.seq_len, p.head_dim
+    sq, sk, sv = _scales(value_scale)
     q = np.empty((B, Hq, N, d), np.float32)
     k = np.empty((B, Hkv, N, d), np.float32)
     v = np.empty((B, Hkv, N, d), np.float32)
     for b in range(B):
         for h in range(Hq):
-            q[b, h] = _to_dtype(_rng(seed, _TQ, b, h).standard_normal((N, d)) * value_scale, p.dtype)
+            q[b, h] = _to_dtype(_rng(seed, _TQ, b, h).standard_normal((N, d)) * sq, p.dtype)
         for h in range(Hkv):
-            k[b, h] = _to_dtype(_rng(seed, _TK, b, h).standard_normal((N, d)) * value_scale, p.dtype)
-            v[b, h] = _to_dtype(_rng(seed, _TV, b, h).standard_normal((N, d)) * value_scale, p.dtype)
+            k[b, h] = _to_dtype(_rng(seed, _TK, b, h).standard_normal((N, d)) * sk, p.dtype)
+            v[b, h] = _to_dtype(_rng(seed, _TV, b, h).standard_normal((N, d)) * sv, p.dtype)
     events = plan_needles(p, seed, plant)
     G, bs = p.group, p.block_size
     noise_rng = {}
@@ -264,15 +274,16 @@ def host_decode_inputs(p: Problem, seed: int, value_scale: float, cache_len: int
     cache_len - 1.
     """
     B, Hq, Hkv, cap, d = p.batch, p.heads_q, p.heads_kv, p.seq_len, p.head_dim
+    sq, sk, sv = _scales(value_scale)
     q = np.empty((B, Hq, d), np.float32)
     k = np.empty((B, Hkv, cap, d), np.float32)
     v = np.empty((B, Hkv, cap, d), np.float32)
     for b in range(B):
         for h in range(Hq):
-            q[b, h] = _to_dtype(_rng(seed, _TQ, b, h).standard_normal(d) * value_scale, p.dtype)
+            q[b, h] = _to_dtype(_rng(seed, _TQ, b, h).standard_normal(d) * sq, p.dtype)
         for h in range(Hkv):
-            k[b, h] = _to_dtype(_rng(seed, _TK, b, h).standard_normal((cap, d)) * value_scale, p.dtype)
-            v[b, h] = _to_dtype(_rng(seed, _TV, b, h).standard_normal((cap, d)) * value_scale, p.dtype)
+            k[b, h] = _to_dtype(_rng(seed, _TK, b, h).standard_normal((cap, d)) * sk, p.dtype)
+            v[b, h] = _to_dtype(_rng(seed, _TV, b, h).standard_normal((cap, d)) * sv, p.dtype)
     events = plan_needles(p.replace(seq_len=cache_len), seed, plant)
     G, bs = p.group, p.block_size
     for (b, g, qb, t) in events:
@@ -321,9 +332,10 @@ def device_inputs(p: Problem, seed: int, value_scale: float, plant=None, device=
     q = torch.empty((B, Hq, N, d), dtype=dt, device=device)
     k = torch.empty((B, Hkv, N, d), dtype=dt, device=device)
     v = torch.empty((B, Hkv, N, d), dtype=dt, device=device)
-    _randn_into(q, device, seed, (_TQ,), value_scale)
-    _randn_into(k, device, seed, (_TK,), value_scale)
-    _randn_into(v, device, seed, (_TV,), value_scale)
+    sq, sk, sv = _scales(value_scale)
+    _randn_into(q, device, seed, (_TQ,), sq)
+    _randn_into(k, device, seed, (_TK,), sk)
+    _randn_into(v, device, seed, (_TV,), sv)
     events = plan_needles(p, seed, plant)
     G, bs = p.group, p.block_size
     gn = _torch_gen(device, seed, _TNOISE)
@@ -345,10 +357,11 @@ def device_decode_inputs(p: Problem, seed: int, value_scale: float, cache_len: i
     q = torch.empty((B, Hq, d), dtype=dt, device=device)
     k = torch.empty((B, Hkv, cap, d), dtype=dt, device=device)
     v = torch.empty((B, Hkv, cap, d), dtype=dt, device=device)
-    _randn_into(q, device, seed, (_TQ,), value_scale)
+    sq, sk, sv = _scales(value_scale)
+    _randn_into(q, device, seed, (_TQ,), sq)
     for b in range(B):  # per sequence, to bound the fp32 temporaries
-        _randn_into(k[b], device, seed, (_TK, b), value_scale)
-        _randn_into(v[b], device, seed, (_TV, b), value_scale)
+        _randn_into(k[b], device, seed, (_TK, b), sk)
+        _randn_into(v[b], device, seed, (_TV, b), sv)
     events = plan_needles(p.replace(seq_len=cache_len), seed, plant)
     G, bs = p.group, p.block_size
     gn = _torch_gen(device, seed, _TNOISE)

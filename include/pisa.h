@@ -1,0 +1,169 @@
+/*
+ * pisa.h -- C ABI of the PISA content-selected block-sparse attention library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are the pages' titles and sections):
+ *
+ *   "Attention clairsemée PISA : noyaux Triton sans matrice de scores"
+ *     - "Une pyramide de clés plutôt qu'un tapis uniforme" and "Le pooling comme
+ *       première réduction": keys are grouped into blocks, blocks into nodes,
+ *       nodes into coarser nodes; each level summarises the level below by
+ *       pooling (here: the arithmetic mean).
+ *     - "La sélection top-K guidée par la pyramide": each query block keeps the
+ *       K most relevant key blocks by descending the levels, pruning at the top
+ *       and refining below, for O(N log N) work.
+ *     - "Des noyaux Triton qui ne matérialisent rien": similarity, selection and
+ *       aggregation never write the N x N score matrix to memory.
+ *   "Dropping the Anchor: ... via Pulsar Attention"
+ *     - "Phase 1 : Encodage statistique du contexte": a small fixed attention-sink
+ *       prefix (64 tokens by default) keeps the softmax stable.
+ *     - "Phase 2 : Encodage de la requête globale": partial attentions over
+ *       disjoint key sets merge exactly with an online softmax.
+ *
+ * Conventions shared by every call:
+ *   - All tensors are caller-owned device memory, contiguous, row-major, 16-byte
+ *     aligned. The library never allocates or frees device memory and keeps no
+ *     mutable global state; calls are thread-safe.
+ *   - Q, K, V, O use the layout [batch, heads, tokens, head_dim] in the problem's
+ *     dtype (fp32 or bf16). The pyramid is fp32 [batch, heads_kv, nodes, head_dim]
+ *     with the levels stored one after another, finest first
+ *     (see pisa_pyramid_layout).
+ *   - Calls are asynchronous on the given HIP stream (0 is the null stream).
+ *     Arguments are validated on the host before anything is launched; on any
+ *     error nothing is launched or written and a non-zero status is returned;
+ *     pisa_last_error() then holds a description (per calling thread). A fault
+ *     inside a kernel surfaces at the caller's next synchronisation.
+ *   - An empty problem (batch == 0 or seq_len == 0) is valid and launches nothing.
+ */
+#ifndef PISA_H
+#define PISA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pisa_status {
+  PISA_OK = 0,
+  PISA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PISA_ERR_SHAPE = 2,       /* sizes are inconsistent or out of range */
+  PISA_ERR_UNSUPPORTED = 3, /* a valid request this version does not implement */
+  PISA_ERR_WORKSPACE = 4,   /* workspace missing or too small */
+  PISA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
+  PISA_ERR_ALIGN = 6        /* a pointer is not 16-byte aligned */
+} pisa_status;
+
+typedef enum pisa_dtype { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
+
+/* Problem description, passed by const pointer to every call.
+ *   heads_q % heads_kv == 0; the G = heads_q / heads_kv query heads of one KV
+ *     head share one selection (grouped-query attention).
+ *   seq_len: N for prefill; the cache capacity for decode. Any N >= 0: a last
+ *     partial block is allowed.
+ *   head_dim: 64 or 128.  block_size: 32, 64 or 128 tokens.
+ *   fanout: 2, 4, 8 or 16 children per pyramid node.
+ *   levels: 1..8 and counts the leaf-block level. The top level may hold at most
+ *     1024 nodes and top_k * fanout + fanout - 1 <= 1024.
+ *   top_k: >= 0 key blocks kept per query block (the beam width at every level).
+ *   sink_len: >= 0 tokens of the always-attended prefix [0, sink_len).
+ *   causal: must be 1 (0 returns PISA_ERR_UNSUPPORTED).
+ *   sm_scale: softmax scale; <= 0 selects 1/sqrt(head_dim).
+ *   dtype: PISA_F32 or PISA_BF16 for Q, K, V and O. */
+typedef struct pisa_problem {
+  int32_t batch;
+  int32_t heads_q;
+  int32_t heads_kv;
+  int32_t head_dim;
+  int64_t seq_len;
+  int32_t block_size;
+  int32_t fanout;
+  int32_t levels;
+  int32_t top_k;
+  int32_t sink_len;
+  int32_t causal;
+  float sm_scale;
+  int32_t dtype;
+} pisa_problem;
+
+/* Node offsets of each pyramid level ("Une pyramide de clés"). Host only, pure.
+ *   level_offsets: host array of levels + 1 entries; entry l is the first node of
+ *   level l within one (batch, kv head) slab, the last entry is the node count
+ *   per slab. Level 0 has ceil(seq_len / block_size) nodes, level l has
+ *   ceil(nodes_{l-1} / fanout). */
+pisa_status pisa_pyramid_layout(const pisa_problem* p, int64_t* level_offsets);
+
+/* Build the key pyramid ("Le pooling comme première réduction").
+ *   k: [batch, heads_kv, seq_len, head_dim] keys.
+ *   pyramid: fp32 [batch, heads_kv, nodes, head_dim], written in full.
+ * Level 0 node j = the mean of key rows [j*bs, min(N, (j+1)*bs)), summed in fp64
+ * and rounded once to fp32; level l node n = the mean of its (up to fanout)
+ * children's stored fp32 values, summed in fp64 and rounded once to fp32. */
+pisa_status pisa_build_pyramid(const pisa_problem* p, const void* k, float* pyramid, hipStream_t stream);
+
+/* Select the top-K key blocks of every query block ("La sélection top-K guidée
+ * par la pyramide").
+ *   q: [batch, heads_q, seq_len, head_dim]; pyramid: from pisa_build_pyramid.
+ *   idx: int32 [batch, heads_kv, n_blocks, top_k], selected blocks in ascending
+ *        order, padded with -1.  cnt: int32 [batch, heads_kv, n_blocks].
+ * The query representative of block qb is the mean of its rows over the G heads
+ * of the KV group (fp64). From the top level down, every node lying wholly
+ * before qb's ancestor at that level and holding at least one block outside the
+ * sink is scored by the fp64 dot product of the representative with its fp32
+ * summary; the K best (score descending, index ascending) are kept, and the next
+ * level's pool is their children plus the complete children of qb's ancestor.
+ * Blocks wholly inside [0, sink_len) and the block qb itself are never
+ * candidates. */
+pisa_status pisa_select_topk(const pisa_problem* p, const void* q, const float* pyramid, int32_t* idx, int32_t* cnt,
+                             hipStream_t stream);
+
+/* Exact softmax attention over the attended set ("Des noyaux Triton qui ne
+ * matérialisent rien"; sink prefix from Pulsar "Phase 1").
+ *   q: [batch, heads_q, seq_len, head_dim]; k, v: [batch, heads_kv, seq_len, head_dim];
+ *   idx, cnt: from pisa_select_topk; out: like q;
+ *   lse: nullable fp32 [batch, heads_q, seq_len], natural-log sum of exp(logits).
+ * Query i of block qb attends to the key set
+ *   ([0, sink_len) U selected blocks of qb U [qb*bs, i]) intersected with [0, i],
+ * each key once, with logits sm_scale * q_i . k_t. No score matrix is written.
+ * bf16 problems use bf16 matrix cores with fp32 accumulation (probabilities are
+ * rounded to bf16 before the value product); fp32 problems compute in fp32. */
+pisa_status pisa_sparse_attn_fwd(const pisa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
+                                 const int32_t* cnt, void* out, float* lse, hipStream_t stream);
+
+/* Device workspace (bytes) that pisa_decode_step needs for this problem. */
+pisa_status pisa_decode_workspace_size(const pisa_problem* p, size_t* bytes);
+
+/* One decode step: a single new query token per sequence whose key and value are
+ * already in the cache at position cache_len - 1 (Pulsar "Phase 2": partial
+ * attentions merged by an online softmax).
+ *   q: [batch, heads_q, head_dim]; k_cache, v_cache: [batch, heads_kv, seq_len, head_dim];
+ *   pyramid: built by pisa_build_pyramid over the cache (nodes past the token's
+ *            own ancestors are never read, so a pyramid of the full capacity works);
+ *   cache_len: 1..seq_len, the same for every sequence;
+ *   out: [batch, heads_q, head_dim]; lse: nullable fp32 [batch, heads_q];
+ *   idx_out: nullable int32 [batch, heads_kv, top_k]; cnt_out: nullable int32 [batch, heads_kv];
+ *   workspace: device memory of at least pisa_decode_workspace_size bytes.
+ * Selection and attended set are those of a one-row query block at position
+ * cache_len - 1. The attended blocks are split across workgroups and the
+ * partial results merged. */
+pisa_status pisa_decode_step(const pisa_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                             const float* pyramid, int64_t cache_len, void* out, float* lse, int32_t* idx_out,
+                             int32_t* cnt_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* pisa_status_string(pisa_status s);
+
+/* Detail of the last failing call on this thread ("" if none). */
+const char* pisa_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t pisa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H */
