@@ -121,10 +121,10 @@ def cpu_baseline(p, q, k, v, seed_units=0):
     t_all = time.perf_counter()
     G, bs, nb = p.group, p.block_size, p.n_blocks
     # the oracle sees one KV head at a time: Q of its group, its K and V
-    n_heads = 2
-    qh = [q[:, g * G:(g + 1) * G].float().cpu().numpy() for g in range(n_heads)]
+    n_heads = p.heads_kv
+    qh = [q[:, g * G:(g + 1) * G].float().cpu().numpy() for g in range(1)]
     kh = [k[:, g:g + 1].float().cpu().numpy() for g in range(n_heads)]
-    vh = [v[:, g:g + 1].float().cpu().numpy() for g in range(n_heads)]
+    vh = [v[:, g:g + 1].float().cpu().numpy() for g in range(1)]
     # stage 1: pyramid of n_heads KV heads (full length)
     t0 = time.perf_counter()
     pyr = [oracle.build_pyramid(kk, bs, p.fanout, p.levels) for kk in kh]
@@ -132,9 +132,9 @@ def cpu_baseline(p, q, k, v, seed_units=0):
     # stage 2: selection of a sample of query blocks
     t0 = time.perf_counter()
     qbar = [oracle.query_block_means(qq, 1, bs) for qq in qh]
-    t_qbar = (time.perf_counter() - t0) / n_heads * p.heads_kv
+    t_qbar = (time.perf_counter() - t0) * p.heads_kv
     rng = np.random.default_rng(seed_units)
-    sel_units = np.sort(rng.choice(nb, 384, replace=False))
+    sel_units = np.sort(rng.choice(nb, min(nb, 1024), replace=False))
     sels = {}
     t0 = time.perf_counter()
     for qb in sel_units:
@@ -142,7 +142,7 @@ def cpu_baseline(p, q, k, v, seed_units=0):
         sels[int(qb)] = oracle.descend(lv, qbar[0][0, 0, qb], int(qb), p.top_k, p.sink_len, bs, p.fanout)
     t_sel = (time.perf_counter() - t0) / len(sel_units) * nb * p.heads_kv + t_qbar
     # stage 3: attention for a sample of units (all G heads, all rows)
-    att_units = sel_units[::8]
+    att_units = sel_units[::2]
     t0 = time.perf_counter()
     for qb in att_units:
         sel = sels[int(qb)]

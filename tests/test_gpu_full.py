@@ -1,0 +1,101 @@
+"""Parity at the workloads' full sizes, in the launch configuration the bench times.
+
+Inputs are drawn on the GPU (gen.device_inputs) and copied to the host for the
+oracle. Every pyramid summary and every selection is compared; attention
+outputs are compared on sampled query blocks (the planted ones, the first and
+last blocks and a seeded random sample), decode on sampled sequences.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import gen
+import oracle
+from parity import (assert_outputs_close, assert_pyramid_equal, assert_selection_equal, cprob, log, split_levels,
+                    to_dev, to_host)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _sample_units(p, man, n_random=12, seed=0):
+    rng = np.random.default_rng(seed)
+    units = set()
+    for n in man["needles"][:12]:
+        units.add((n["b"], n["g"], n["qb"]))
+    nb = p.n_blocks
+    for g in range(min(p.heads_kv, 2)):
+        units.update({(0, g, 0), (0, g, 1), (0, g, nb - 1)})
+    for _ in range(n_random):
+        units.add((int(rng.integers(p.batch)), int(rng.integers(p.heads_kv)), int(rng.integers(nb))))
+    return sorted(units)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 5])
+def test_full_prefill(cfg_id):
+    import block_sparse_long_pisa_amd as pisa
+
+    c = gen.config(cfg_id)
+    p = c["problem"]
+    log(f"config {cfg_id}: {c['name']}")
+    if cfg_id == 1:
+        qh, kh, vh, man = gen.host_inputs(p, c["seed"], c["value_scale"], c["plant"])
+        q, k, v = to_dev(qh, p.dtype), to_dev(kh, p.dtype), to_dev(vh, p.dtype)
+    else:
+        q, k, v, man = gen.device_inputs(p, c["seed"], c["value_scale"], c["plant"], device="cuda")
+    cp = cprob(p)
+    out, lse, idx, cnt, pyr = pisa.prefill(cp, q, k, v, want_lse=True)
+    torch.cuda.synchronize()
+    offs = pisa.pyramid_layout(cp)
+    g_levels = split_levels(to_host(pyr), offs)
+    gi, gc = to_host(idx), to_host(cnt)
+    del pyr
+    if cfg_id != 1:
+        qh, kh, vh = to_host(q), to_host(k), to_host(v)
+    log("  GPU done; oracle pyramid")
+    o_levels = oracle.build_pyramid(kh, p.block_size, p.fanout, p.levels)
+    assert_pyramid_equal(g_levels, o_levels)
+    log("  pyramid bit-exact; oracle selection of every query block")
+    qbar = oracle.query_block_means(qh, p.heads_kv, p.block_size)
+    oi, oc = oracle.select(o_levels, qbar, p.top_k, p.sink_len, p.block_size, p.fanout)
+    assert_selection_equal(gi, gc, oi, oc)
+    log(f"  {oc.size} selections bit-exact; oracle attention on sampled blocks")
+    units = _sample_units(p, man) if cfg_id != 1 else None
+    o, ol = oracle.attend(qh, kh, vh, oi, oc, p.sink_len, p.block_size, p.scale, blocks=units)
+    err = assert_outputs_close(p, to_host(out), o, to_host(lse), ol)
+    found = sum(1 for n in man["needles"] if n["survived"] and n["target"] in oi[n["b"], n["g"], n["qb"]].tolist())
+    log(f"  max abs err {err:.2e}; planted blocks selected: {found}/{sum(n['survived'] for n in man['needles'])}")
+
+
+@pytest.mark.timeout(900)
+def test_full_decode():
+    import block_sparse_long_pisa_amd as pisa
+
+    c = gen.config(4)
+    p = c["problem"]
+    cache_len = p.seq_len
+    log(f"config 4: {c['name']}")
+    q, kc, vc, man = gen.device_decode_inputs(p, c["seed"], c["value_scale"], cache_len, device="cuda")
+    cp = cprob(p)
+    pyr = pisa.build_pyramid(cp, kc)
+    out, lse, idx, cnt = pisa.decode_step(cp, q, kc, vc, pyr, cache_len, want_lse=True, want_idx=True)
+    torch.cuda.synchronize()
+    offs = pisa.pyramid_layout(cp)
+    qh = to_host(q)
+    oh, lh, gi, gc = to_host(out), to_host(lse), to_host(idx), to_host(cnt)
+    for b in (0, 17, 42, 63):
+        log(f"  sequence {b}")
+        kb, vb = to_host(kc[b:b + 1]), to_host(vc[b:b + 1])
+        g_levels = split_levels(to_host(pyr[b:b + 1]), offs)
+        o_levels = oracle.build_pyramid(kb, p.block_size, p.fanout, p.levels)
+        assert_pyramid_equal(g_levels, o_levels)
+        o, ol, oi, oc = oracle.decode(qh[b:b + 1], kb, vb, o_levels, cache_len, p.top_k, p.sink_len, p.block_size,
+                                      p.fanout, p.scale)
+        assert np.array_equal(gc[b:b + 1], oc) and np.array_equal(gi[b:b + 1], oi)
+        err = assert_outputs_close(p, oh[b:b + 1], o, lh[b:b + 1], ol)
+        planted = [n for n in man["needles"] if n["b"] == b]
+        found = sum(1 for n in planted if n["target"] in oi[0, n["g"]].tolist())
+        log(f"    max abs err {err:.2e}; planted blocks selected {found}/{len(planted)}")
