@@ -12,10 +12,12 @@
 //
 // bf16 path: one workgroup serves up to 8 waves x 32 query rows of one
 // (batch, kv head, query block) unit -- rows of all heads in the GQA group --
-// so every K/V tile staged in LDS feeds up to 256 rows. Per tile each wave
-// computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (a lane then owns one
-// query column), runs the online softmax in registers, and accumulates
-// O^T += V^T P^T on the same matrix cores, with V stored transposed in LDS.
+// so every K/V tile staged in LDS feeds up to 256 rows. Tiles arrive by
+// asynchronous global->LDS copies into two stages, the next tile in flight while
+// the current one is computed. Per tile each wave computes S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 (a lane then owns one query column), runs the
+// online softmax in registers, and accumulates O^T += V^T P^T on the same
+// matrix cores, reading V^T fragments with gfx950's transposing LDS reads.
 // fp32 path: plain VALU, one thread per query row.
 #include "pisa_internal.h"
 
@@ -27,6 +29,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+// 2^x with the hardware's v_exp_f32 and no denormal range reduction: results
+// below 2^-126 only ever weigh a softmax term that is negligible anyway.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Which key block a tile index refers to, and how many of its keys count.
 struct TileWalk {
@@ -68,8 +74,144 @@ __device__ __forceinline__ TileWalk make_walk(const Geo& g, int qb, const int* s
   return w;
 }
 
-__device__ __forceinline__ uint32_t word(const uint4& u, int p) {
-  return p == 0 ? u.x : (p == 1 ? u.y : (p == 2 ? u.z : u.w));
+// LDS tiles hold key rows of D bf16 as 16-byte chunks; chunk cc of row r sits at
+// chunk position cc ^ swz(r). The swizzle keeps the two read patterns free of
+// bank conflicts: 16 consecutive rows at one chunk (K fragments of S^T = K Q^T)
+// and 4 consecutive rows x 4 consecutive chunks (transposing V^T reads).
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
+
+// Issue the asynchronous global->LDS copies of one K and one V tile (block j).
+// Each wave instruction fills 64 consecutive 16-byte LDS chunks; rows past the
+// end of the sequence re-read the last valid row (their keys are masked).
+template <int D, int BS, int NW>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
+                                           int rows_in_mem, uint16_t* kdst, uint16_t* vdst, int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int INSTR = BS * CPR / 64;
+  for (int i = wave; i < INSTR; i += NW) {
+    const int u = i * 64 + lane;
+    const int r = u / CPR;
+    const int cc = (u % CPR) ^ swz<CPR>(r);
+    const int gr = min(r, rows_in_mem - 1);
+    __builtin_amdgcn_global_load_lds(kt + gr * D + cc * 8, (lds_void_ptr)(kdst + i * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vt + gr * D + cc * 8, (lds_void_ptr)(vdst + i * 512), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_loads_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0) only (expcnt, lgkmcnt left free)
+  __syncthreads();                            // ... and every other wave's
+}
+
+template <int D, int BS>
+struct AttnState {
+  static constexpr int NKB = BS / 32;
+  static constexpr int NDS = D / 16;
+  static constexpr int NDB = D / 32;
+  bf16x8_t qf[NDS];
+  f32x16_t oacc[NDB];
+  float m_run, l_run;
+  int offk[NDS];      // byte offsets of this lane's K-fragment chunks
+  int offv[2][NDB];   // byte offsets of this lane's V^T transposing reads
+};
+
+// One key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T, in chunks of
+// at most 64 keys (32 live accumulator registers for S per chunk).
+template <int D, int BS>
+__device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_t* ks, const uint16_t* vs, int nvalid,
+                                             bool local, int key0, int qpos, int hi, float c) {
+  constexpr int CPR = D / 8;
+  constexpr int NDS = D / 16, NDB = D / 32;
+  constexpr int KC = BS < 64 ? BS : 64;  // keys per chunk
+  constexpr int NKB = KC / 32;
+  const char* kb_base = reinterpret_cast<const char*>(ks);
+  const char* vb_base = reinterpret_cast<const char*>(vs);
+#pragma unroll
+  for (int ch = 0; ch < BS / KC; ++ch) {
+    f32x16_t sacc[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const bf16x8_t a =
+            *reinterpret_cast<const bf16x8_t*>(kb_base + st.offk[ds] + (ch * KC + kb * 32) * CPR * 16);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[ds], sacc[kb], 0, 0, 0);
+      }
+    }
+    if (__builtin_expect(local || nvalid < BS, 0)) {  // uniform across the workgroup
+      // keys of this tile beyond `lim` are masked (partial block, causal diagonal)
+      const int lim = min(nvalid - 1, local ? qpos - key0 : BS - 1) - (ch * KC + hi * 4);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -__builtin_inff();
+    }
+    // online softmax in the log2 domain; the reference max only moves when the
+    // chunk max exceeds it by more than 8 (a factor 2^8), then O and l rescale
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mt = mx * c;
+    const bool move = mt > st.m_run + 8.f;
+    const float m_ref = move ? mt : st.m_run;
+    const float m_use = m_ref == -__builtin_inff() ? 0.f : m_ref;
+    if (__any(move)) {
+      const float alpha = fast_exp2(st.m_run - m_use);
+      st.l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st.oacc[db][i] *= alpha;
+    }
+    st.m_run = m_ref;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(sacc[kb][i], c, -m_use));
+        sacc[kb][i] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 32);
+    st.l_run += rs;
+    // O^T[d][query] += V^T P^T over 16-key steps; slot (hi, e) of step (kb, hh)
+    // holds key kb*32 + hh*16 + (e/4)*8 + hi*4 + e%4
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][hh * 8 + e];
+        const int step = (ch * KC + kb * 32 + hh * 16) * CPR * 16;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const v4i16_t lo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vb_base + st.offv[0][db] + step));
+          const v4i16_t up =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vb_base + st.offv[1][db] + step));
+          const v4i16_t a8[2] = {lo, up};
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a8);
+          st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, st.oacc[db], 0, 0, 0);
+        }
+      }
+    }
+  }
 }
 
 template <int D, int BS, int NW>
@@ -80,13 +222,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
                                                             const int32_t* __restrict__ cnt, uint16_t* __restrict__ out,
                                                             float* __restrict__ lse, int parts) {
   constexpr int NT = NW * 64;
-  constexpr int KP = D + 8;   // K tile row pitch (bf16): 16-lane groups hit distinct banks
-  constexpr int VP = BS + 4;  // V^T tile row pitch (bf16)
-  constexpr int NKB = BS / 32;
+  constexpr int CPR = D / 8;
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BS * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  // two stages of K and V tiles, filled by asynchronous copies
+  __shared__ __attribute__((aligned(16))) uint16_t K0[BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[BS * D];
   __shared__ int sel[kMaxTopK];
 
   // heaviest units first; consecutive workgroups walk the (batch, kv head) slabs
@@ -112,22 +255,34 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
   const int nsel = min(max(cnt[unit], 0), g.K);
   for (int t = threadIdx.x; t < nsel; t += NT) sel[t] = idx[unit * g.K + t];
 
-  bf16x8_t qf[NDS];
+  AttnState<D, BS> st;
   {
     const uint16_t* qrow = q + (((int64_t)b * g.Hq + h) * g.N + (qvalid ? qpos : 0)) * D;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
       uint4 u = qvalid ? *reinterpret_cast<const uint4*>(qrow + ds * 16 + hi * 8) : make_uint4(0, 0, 0, 0);
-      qf[ds] = __builtin_bit_cast(bf16x8_t, u);
+      st.qf[ds] = __builtin_bit_cast(bf16x8_t, u);
     }
   }
-  f32x16_t oacc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+    for (int i = 0; i < 16; ++i) st.oacc[db][i] = 0.f;
+  st.m_run = -__builtin_inff();
+  st.l_run = 0.f;
+  {
+    const int gk = swz<CPR>(l32);
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) st.offk[ds] = (l32 * CPR + ((2 * ds + hi) ^ gk)) * 16;
+    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+      const int rr = hi * 4 + ((lane & 15) >> 2) + 8 * sec;
+      const int x = cl ^ swz<CPR>(rr);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) st.offv[sec][db] = (rr * CPR + ((4 * db) ^ x)) * 16 + (lane & 1) * 8;
+    }
+  }
   const float c = g.scale * kLog2e;
 
   const uint16_t* kbase = k + ((int64_t)b * g.Hkv + kvh) * g.N * D;
@@ -135,121 +290,35 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
   __syncthreads();
   const TileWalk walk = make_walk(g, qb, sel, nsel);
 
-  for (int t = 0; t < walk.ntiles; ++t) {
-    int j, nvalid;
-    bool local;
-    walk.at(t, sel, g, qb, local_rows, j, nvalid, local);
-    const int rows_in_mem = min(BS, g.N - j * BS);
-    const uint16_t* kt = kbase + (int64_t)j * BS * D;
-    const uint16_t* vt = vbase + (int64_t)j * BS * D;
-
-    // stage K (row-major) and V (transposed) in LDS
-    for (int ci = threadIdx.x; ci < BS * D / 8; ci += NT) {
-      const int row = ci / (D / 8);
-      const int cc = ci % (D / 8);
-      uint4 u = row < rows_in_mem ? *reinterpret_cast<const uint4*>(kt + row * D + cc * 8) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(Ks + row * KP + cc * 8) = u;
+  int j, nvalid;
+  bool local;
+  walk.at(0, sel, g, qb, local_rows, j, nvalid, local);
+  issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
+                        wave, lane);
+  for (int t = 0; t < walk.ntiles; t += 2) {
+    // even tile: compute from stage 0 while stage 1 fills
+    wait_loads_and_sync();
+    int j1 = 0, nv1 = 0;
+    bool loc1 = false;
+    if (t + 1 < walk.ntiles) {
+      walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
+      issue_tile<D, BS, NW>(kbase + (int64_t)j1 * BS * D, vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K1,
+                            V1, wave, lane);
     }
-    for (int vb = threadIdx.x; vb < (BS / 4) * (D / 8); vb += NT) {
-      const int kg = vb / (D / 8);
-      const int dg = vb % (D / 8);
-      uint4 r[4];
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = kg * 4 + rr;
-        r[rr] = row < rows_in_mem ? *reinterpret_cast<const uint4*>(vt + row * D + dg * 8) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w0 = word(r[0], e >> 1), w1 = word(r[1], e >> 1);
-        const uint32_t w2 = word(r[2], e >> 1), w3 = word(r[3], e >> 1);
-        uint2 o2;
-        if (e & 1) {
-          o2.x = (w0 >> 16) | (w1 & 0xffff0000u);
-          o2.y = (w2 >> 16) | (w3 & 0xffff0000u);
-        } else {
-          o2.x = (w0 & 0xffffu) | (w1 << 16);
-          o2.y = (w2 & 0xffffu) | (w3 << 16);
-        }
-        *reinterpret_cast<uint2*>(Vt + (dg * 8 + e) * VP + kg * 4) = o2;
-      }
+    compute_tile<D, BS>(st, K0, V0, nvalid, local, j * BS, qpos, hi, c);
+    if (t + 1 >= walk.ntiles) break;
+    // odd tile: compute from stage 1 while stage 0 fills
+    wait_loads_and_sync();
+    if (t + 2 < walk.ntiles) {
+      walk.at(t + 2, sel, g, qb, local_rows, j, nvalid, local);
+      issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
+                            wave, lane);
     }
-    __syncthreads();
-
-    // S^T[key][query] for 32-key blocks; lane (l32, hi) owns query l32 and keys
-    // kb*32 + (i/4)*8 + hi*4 + i%4 of accumulator element i
-    f32x16_t sacc[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(Ks + (kb * 32 + l32) * KP + ds * 16 + hi * 8);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sacc[kb], 0, 0, 0);
-      }
-    }
-    if (local || nvalid < BS) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb * 32 + (i >> 2) * 8 + hi * 4 + (i & 3);
-          const bool ok = key < nvalid && (!local || j * BS + key <= qpos);
-          if (!ok) sacc[kb][i] = -__builtin_inff();
-        }
-    }
-    // online softmax (log2 domain)
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = exp2f(fmaf(sacc[kb][i], c, -m_use));
-        sacc[kb][i] = p;
-        rs += p;
-      }
-    rs += __shfl_xor(rs, 32);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-
-    // O^T[d][query] += V^T P^T over 16-key steps; B-operand slot (hi, e) of step
-    // (kb, hh) holds key kb*32 + hh*16 + (e/4)*8 + hi*4 + e%4
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8_t pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][hh * 8 + e];
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const uint16_t* vp = Vt + (db * 32 + l32) * VP + kb * 32 + hh * 16 + hi * 4;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-          const uint2 up = *reinterpret_cast<const uint2*>(vp + 8);
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, up.x, up.y));
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();
+    compute_tile<D, BS>(st, K1, V1, nv1, loc1, j1 * BS, qpos, hi, c);
   }
 
   if (qvalid) {
-    const float inv = 1.f / l_run;
+    const float inv = 1.f / st.l_run;
     uint16_t* orow = out + (((int64_t)b * g.Hq + h) * g.N + qpos) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -257,11 +326,11 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
       for (int i = 0; i < 16; i += 4) {
         const int d = db * 32 + (i >> 2) * 8 + hi * 4;
         uint2 w;
-        w.x = pack_bf16x2(oacc[db][i] * inv, oacc[db][i + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][i + 2] * inv, oacc[db][i + 3] * inv);
+        w.x = pack_bf16x2(st.oacc[db][i] * inv, st.oacc[db][i + 1] * inv);
+        w.y = pack_bf16x2(st.oacc[db][i + 2] * inv, st.oacc[db][i + 3] * inv);
         *reinterpret_cast<uint2*>(orow + d) = w;
       }
-    if (lse != nullptr && hi == 0) lse[((int64_t)b * g.Hq + h) * g.N + qpos] = (m_run + log2f(l_run)) * kLn2;
+    if (lse != nullptr && hi == 0) lse[((int64_t)b * g.Hq + h) * g.N + qpos] = (st.m_run + log2f(st.l_run)) * kLn2;
   }
 }
 
