@@ -166,29 +166,13 @@ def cpu_baseline(p, q, k, v, seed_units=0):
 # ---------------------------------------------------------------------------
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode-steps", type=int, default=50)
-    ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
-    args = ap.parse_args(argv)
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no multi-GPU path", flush=True)
-        return 2
-
+def run_prefill(args, dev):
     import numpy as np
     import torch
 
     import block_sparse_long_pisa_amd as pisa
     import gen
 
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     cfg = gen.config(3)
     p = cfg["problem"]
     cp = pisa.problem(p.batch, p.heads_q, p.heads_kv, p.seq_len, p.head_dim, p.block_size, p.fanout, p.levels,
@@ -299,45 +283,87 @@ def main(argv=None):
     del q, k, v, out, pyr
     torch.cuda.empty_cache()
 
-    if not args.no_decode:
-        dcfg = gen.config(4)
-        dp = dcfg["problem"]
-        dcp = pisa.problem(dp.batch, dp.heads_q, dp.heads_kv, dp.seq_len, dp.head_dim, dp.block_size, dp.fanout,
-                           dp.levels, dp.top_k, dp.sink_len, dp.dtype)
-        cache_len = dp.seq_len
-        log(f"generating {dcfg['name']} on the GPU")
-        dq, kc, vc, _ = gen.device_decode_inputs(dp, dcfg["seed"], dcfg["value_scale"], cache_len, device=dev)
-        dpyr = pisa.build_pyramid(dcp, kc)  # built once over the cache, not timed
-        ws = torch.empty(pisa.decode_workspace_size(dcp), dtype=torch.uint8, device=dev)
-        dout = torch.empty_like(dq)
-        didx = torch.empty((dp.batch, dp.heads_kv, dp.top_k), dtype=torch.int32, device=dev)
-        dcnt = torch.empty((dp.batch, dp.heads_kv), dtype=torch.int32, device=dev)
-        for _ in range(args.warmup):
-            pisa.decode_step(dcp, dq, kc, vc, dpyr, cache_len, out=dout, idx_out=didx, cnt_out=dcnt, workspace=ws)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        e0.record()
-        for _ in range(args.decode_steps):
-            pisa.decode_step(dcp, dq, kc, vc, dpyr, cache_len, out=dout, idx_out=didx, cnt_out=dcnt, workspace=ws)
-        e1.record()
-        torch.cuda.synchronize()
-        t_dec = (time.perf_counter() - t0) / args.decode_steps
-        t_dec_ev = e0.elapsed_time(e1) * 1e-3 / args.decode_steps
-        db = decode_bytes(dp, cache_len, dcnt.cpu().numpy())
-        log(f"decode {t_dec * 1e6:.1f} us/step ({db / t_dec_ev / 1e9:.0f} GB/s)")
-        result["decode"] = {
-            "workload": "PISA decode, bf16 GQA 32q/8kv, 64 sequences x 131072-token cache, one new token each, "
-                        "block 128, fanout 8, 4 levels, K=32, 64-token sink",
-            "us_per_step": t_dec * 1e6,
-            "us_per_step_events": t_dec_ev * 1e6,
-            "tokens_per_s": dp.batch / t_dec,
-            "steps": args.decode_steps,
-            "bound": "hbm",
-            "bytes_per_step": db,
-            "GB/s": db / t_dec_ev / 1e9,
-            "frac": db / t_dec_ev / HBM_PEAK,
-        }
+    return result
+
+
+def run_decode(args, dev):
+    import torch
+
+    import block_sparse_long_pisa_amd as pisa
+    import gen
+
+    dcfg = gen.config(4)
+    dp = dcfg["problem"]
+    dcp = pisa.problem(dp.batch, dp.heads_q, dp.heads_kv, dp.seq_len, dp.head_dim, dp.block_size, dp.fanout,
+                       dp.levels, dp.top_k, dp.sink_len, dp.dtype)
+    cache_len = dp.seq_len
+    log(f"generating {dcfg['name']} on the GPU")
+    dq, kc, vc, _ = gen.device_decode_inputs(dp, dcfg["seed"], dcfg["value_scale"], cache_len, device=dev)
+    dpyr = pisa.build_pyramid(dcp, kc)  # built once over the cache, not timed
+    ws = torch.empty(pisa.decode_workspace_size(dcp), dtype=torch.uint8, device=dev)
+    dout = torch.empty_like(dq)
+    didx = torch.empty((dp.batch, dp.heads_kv, dp.top_k), dtype=torch.int32, device=dev)
+    dcnt = torch.empty((dp.batch, dp.heads_kv), dtype=torch.int32, device=dev)
+    for _ in range(args.warmup):
+        pisa.decode_step(dcp, dq, kc, vc, dpyr, cache_len, out=dout, idx_out=didx, cnt_out=dcnt, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.decode_steps):
+        pisa.decode_step(dcp, dq, kc, vc, dpyr, cache_len, out=dout, idx_out=didx, cnt_out=dcnt, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    t_dec = (time.perf_counter() - t0) / args.decode_steps
+    t_dec_ev = e0.elapsed_time(e1) * 1e-3 / args.decode_steps
+    db = decode_bytes(dp, cache_len, dcnt.cpu().numpy())
+    log(f"decode {t_dec * 1e6:.1f} us/step ({db / t_dec_ev / 1e9:.0f} GB/s)")
+    decode = {
+        "workload": "PISA decode, bf16 GQA 32q/8kv, 64 sequences x 131072-token cache, one new token each, "
+                    "block 128, fanout 8, 4 levels, K=32, 64-token sink",
+        "us_per_step": t_dec * 1e6,
+        "us_per_step_events": t_dec_ev * 1e6,
+        "tokens_per_s": dp.batch / t_dec,
+        "steps": args.decode_steps,
+        "bound": "hbm",
+        "bytes_per_step": db,
+        "GB/s": db / t_dec_ev / 1e9,
+        "frac": db / t_dec_ev / HBM_PEAK,
+    }
+    return decode
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="run one workload only (profiling); the JSON line then lacks the other")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no multi-GPU path", flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_sparse_long_pisa_amd as pisa
+    import gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.only == "decode":
+        result = {"metric": "decode µs/step (profiling run)", "decode": run_decode(args, dev)}
+    else:
+        result = run_prefill(args, dev)
+        if not args.no_decode and args.only is None:
+            result["decode"] = run_decode(args, dev)
     print(json.dumps(result), flush=True)
     return 0
 

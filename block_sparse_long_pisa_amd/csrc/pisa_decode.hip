@@ -33,17 +33,22 @@ struct DecodeWs {
   float* o;      // [B*Hkv, S, G, D] unnormalised
 };
 
+// One workgroup of 512 threads per (batch, kv head): mean of the group's query
+// rows, then the descent with each level's pool scored in few rounds of loads
+// (the decode pyramid comes from HBM) and ranked by counting.
+constexpr int kDecSelThreads = 512;
+
 template <typename T, int D>
-__global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(Geo g, const T* __restrict__ q,
+__global__ __launch_bounds__(kDecSelThreads) void decode_select_kernel(Geo g, const T* __restrict__ q,
                                                                        const float* __restrict__ pyr, int qb,
                                                                        int32_t* __restrict__ idx,
                                                                        int32_t* __restrict__ cnt) {
+  __shared__ BlockSmem smem;
   __shared__ double qbar[D];
-  __shared__ DescentSmem sm;
   const int slab = blockIdx.x;
   const int b = slab / g.Hkv;
   const int kvh = slab % g.Hkv;
-  for (int c = threadIdx.x; c < D; c += kSelectThreads) {
+  for (int c = threadIdx.x; c < D; c += kDecSelThreads) {
     double s = 0.0;
     for (int hh = 0; hh < g.G; ++hh) {
       const T* row = q + ((int64_t)b * g.Hq + kvh * g.G + hh) * D;
@@ -55,7 +60,8 @@ __global__ __launch_bounds__(kSelectThreads) void decode_select_kernel(Geo g, co
     qbar[c] = s / (double)g.G;
   }
   __syncthreads();
-  descend<D>(g, pyr + (int64_t)slab * g.off[g.L] * D, qbar, qb, idx + (int64_t)slab * g.K, cnt + slab, sm);
+  block_descend<D, kDecSelThreads, 8>(g, pyr + (int64_t)slab * g.off[g.L] * D, qb, qbar,
+                                      idx + (int64_t)slab * g.K, cnt + slab, smem);
 }
 
 // Block walk of the decode token (position pos, block qb): full sink blocks,
@@ -85,6 +91,40 @@ __device__ __forceinline__ int decode_ntiles(const Geo& g, int qb, const int* se
   return min(g.j0, qb) + (tail ? 1 : 0) + nsel + 1;
 }
 
+// Sum v[0, C) over the lanes of an aligned group of 2*S lanes (xor butterfly),
+// halving the values each step: afterwards lane i of the group holds the sums
+// of values [first, first + C / (2S)) with first = sum over steps of
+// bit(i, s) * (half at that step). Once one value is left it is summed whole.
+template <int C, int S>
+__device__ __forceinline__ void butterfly(float* v, int lane) {
+  if constexpr (S >= 1) {
+    if constexpr (C > 1) {
+      constexpr int H = C / 2;
+      const bool up = (lane & S) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float send = up ? v[i] : v[i + H];
+        const float keep = up ? v[i + H] : v[i];
+        v[i] = keep + __shfl_xor(send, S);
+      }
+      butterfly<H, S / 2>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], S);
+      butterfly<1, S / 2>(v, lane);
+    }
+  }
+}
+
+// Index of the first value a lane holds after butterfly<C, S>.
+template <int C, int S>
+__device__ __forceinline__ int butterfly_first(int lane) {
+  if constexpr (S >= 1 && C > 1) {
+    return ((lane & S) ? C / 2 : 0) + butterfly_first<C / 2, S / 2>(lane);
+  } else {
+    return 0;
+  }
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T* __restrict__ q,
                                                                   const T* __restrict__ kc, const T* __restrict__ vc,
@@ -93,11 +133,14 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T
   constexpr int LPR = D / VEC;                // lanes per cache row
   constexpr int RP = kDecThreads / LPR;       // rows per pass of the workgroup
   constexpr int MAXK = kTilesPerSplit * 128;  // keys per split (bs <= 128)
+  constexpr int RPT = 128 / RP;               // rows per thread per 128-key tile
+  constexpr int NV = RPT * G;                 // partial dots per thread per tile
+  constexpr int HOLD = NV >= LPR ? NV / LPR : 1;
   __shared__ float qs[G][D];
-  __shared__ float sc[MAXK][G];  // logits (log2 domain) of this split's keys
+  __shared__ float sc[MAXK][G];  // logits, then weights 2^(logit - max), of this split's keys
   __shared__ int sel[kMaxTopK];
   __shared__ float red[kDecThreads / 64][G][D];
-  __shared__ float mred[G];
+  __shared__ float mred[kDecThreads / 64][G];
 
   const int split = blockIdx.x;
   const int slab = blockIdx.y;
@@ -108,7 +151,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T
   const int wave = tid >> 6;
   const int col = (tid % LPR) * VEC;
   const int rsub = tid / LPR;
-  const int nsel = ws.cnt[slab];
+  const int nsel = min(max(ws.cnt[slab], 0), g.K);
   for (int t = tid; t < nsel; t += kDecThreads) sel[t] = ws.idx[(int64_t)slab * g.K + t];
   for (int e = tid; e < G * D; e += kDecThreads) {
     const T* row = q + ((int64_t)b * g.Hq + kvh * G + e / D) * D;
@@ -130,48 +173,77 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T
   const T* vb = vc + (int64_t)slab * g.N * D;
   const float c = g.scale * kLog2e;
 
-  // pass 1: logits of every key of this split
+  // pass 1: logits of every key of this split; all of a tile's loads first
   int nkeys = 0;
   for (int t = t0; t < t1; ++t) {
     int j, nvalid;
     decode_tile(g, qb, pos, sel, nsel, t, j, nvalid);
-    for (int r = rsub; r < g.bs; r += RP) {
-      float x[VEC];
-      const bool in = r < nvalid;
-      if (in) Wide<T>::load(kb + ((int64_t)j * g.bs + r) * D + col, x);
-      float part[G];
+    float x[RPT][VEC];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)  // unconditional loads (clamped rows): all in flight
+      Wide<T>::load(kb + ((int64_t)j * g.bs + min(rsub + i * RP, nvalid - 1)) * D + col, x[i]);
+    float part[NV];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float s = 0.f;
-        if (in) {
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) s = fmaf(qr[hh][e], x[e], s);
-        }
-        part[hh] = s;
+        for (int e = 0; e < VEC; ++e) s = fmaf(qr[hh][e], x[i][e], s);
+        part[i * G + hh] = s;
       }
+    butterfly<NV, LPR / 2>(part, lane);
+    const int first = butterfly_first<NV, LPR / 2>(lane);
+    // with fewer sums than lanes, aligned runs of LPR / NV lanes hold the same sum
+    if ((tid % (NV >= LPR ? 1 : LPR / NV)) == 0) {
 #pragma unroll
-      for (int sh = 1; sh < LPR; sh <<= 1)
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) part[hh] += __shfl_xor(part[hh], sh);
-      if ((tid % LPR) == 0) {
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) sc[nkeys + r][hh] = in ? part[hh] * c : -__builtin_inff();
+      for (int e = 0; e < HOLD; ++e) {
+        const int v = first + e;
+        const int r = rsub + (v / G) * RP;
+        if (r < g.bs) sc[nkeys + r][v % G] = r < nvalid ? part[e] * c : -__builtin_inff();
       }
     }
     nkeys += g.bs;
   }
   __syncthreads();
-  // per-head max over the split
-  if (tid < G) {
-    float mx = -__builtin_inff();
-    for (int r = 0; r < nkeys; ++r) mx = fmaxf(mx, sc[r][tid]);
-    mred[tid] = mx;
+  // per-head max over the split, then the weights in place and their sums
+  float mx[G], ls[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) mx[hh] = -__builtin_inff();
+  for (int r = tid; r < nkeys; r += kDecThreads)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) mx[hh] = fmaxf(mx[hh], sc[r][hh]);
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) mx[hh] = fmaxf(mx[hh], __shfl_xor(mx[hh], sh));
+    if (lane == 0) mred[wave][hh] = mx[hh];
   }
   __syncthreads();
-  float mh[G];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) mh[hh] = mred[hh] == -__builtin_inff() ? 0.f : mred[hh];
-  // pass 2: stream V once, weights exp2(logit - max)
+  for (int hh = 0; hh < G; ++hh) {
+    float m = mred[0][hh];
+#pragma unroll
+    for (int w = 1; w < kDecThreads / 64; ++w) m = fmaxf(m, mred[w][hh]);
+    mx[hh] = m;
+    ls[hh] = 0.f;
+  }
+  __syncthreads();  // everyone has read mred before it is reused for the sums
+  for (int r = tid; r < nkeys; r += kDecThreads)
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float p = mx[hh] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(sc[r][hh] - mx[hh]);
+      sc[r][hh] = p;
+      ls[hh] += p;
+    }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) ls[hh] += __shfl_xor(ls[hh], sh);
+    if (lane == 0) mred[wave][hh] = ls[hh];
+  }
+  __syncthreads();
+  // pass 2: stream V once, all of a tile's loads first
   float acc[G][VEC];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh)
@@ -181,14 +253,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T
   for (int t = t0; t < t1; ++t) {
     int j, nvalid;
     decode_tile(g, qb, pos, sel, nsel, t, j, nvalid);
-    for (int r = rsub; r < nvalid; r += RP) {
-      float x[VEC];
-      Wide<T>::load(vb + ((int64_t)j * g.bs + r) * D + col, x);
+    float x[RPT][VEC];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)  // unconditional loads (clamped rows): all in flight
+      Wide<T>::load(vb + ((int64_t)j * g.bs + min(rsub + i * RP, nvalid - 1)) * D + col, x[i]);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rsub + i * RP;
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        const float p = exp2f(sc[base + r][hh] - mh[hh]);
+        const float p = r < nvalid ? sc[base + min(r, g.bs - 1)][hh] : 0.f;
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[hh][e] = fmaf(p, x[e], acc[hh][e]);
+        for (int e = 0; e < VEC; ++e) acc[hh][e] = fmaf(p, x[i][e], acc[hh][e]);
       }
     }
     base += g.bs;
@@ -217,8 +293,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T
   }
   if (tid < G) {
     float l = 0.f;
-    for (int r = 0; r < nkeys; ++r) l += exp2f(sc[r][tid] - mh[tid]);
-    ws.m[pbase + tid] = mred[tid];
+#pragma unroll
+    for (int w = 0; w < kDecThreads / 64; ++w) l += mred[w][tid];
+    ws.m[pbase + tid] = mx[tid];
     ws.l[pbase + tid] = l;
   }
 }
@@ -290,7 +367,7 @@ static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, c
   const int slabs = g.B * g.Hkv;
   const int pos = cache_len - 1;
   const int qb = pos / g.bs;
-  hipLaunchKernelGGL((decode_select_kernel<T, D>), dim3(slabs), dim3(kSelectThreads), 0, s, g, (const T*)q, pyr, qb,
+  hipLaunchKernelGGL((decode_select_kernel<T, D>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, (const T*)q, pyr, qb,
                      ws.idx, ws.cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

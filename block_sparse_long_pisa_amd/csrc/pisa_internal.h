@@ -47,24 +47,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Load 16 bytes and widen to fp32: 8 values for bf16, 4 for fp32.
 template <typename T>
 struct Wide;
+// raw() fetches the 16 bytes, widen() converts them: issuing several raw()
+// before any widen() keeps the loads in flight together.
 template <>
 struct Wide<uint16_t> {
   static constexpr int kVec = 8;
-  __device__ __forceinline__ static void load(const uint16_t* p, float* out) {
-    uint4 u = *reinterpret_cast<const uint4*>(p);
+  __device__ __forceinline__ static uint4 raw(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static void widen(const uint4& u, float* out) {
     out[0] = bf16lo(u.x); out[1] = bf16hi(u.x);
     out[2] = bf16lo(u.y); out[3] = bf16hi(u.y);
     out[4] = bf16lo(u.z); out[5] = bf16hi(u.z);
     out[6] = bf16lo(u.w); out[7] = bf16hi(u.w);
   }
+  __device__ __forceinline__ static void load(const uint16_t* p, float* out) { widen(raw(p), out); }
 };
 template <>
 struct Wide<float> {
   static constexpr int kVec = 4;
-  __device__ __forceinline__ static void load(const float* p, float* out) {
-    float4 u = *reinterpret_cast<const float4*>(p);
-    out[0] = u.x; out[1] = u.y; out[2] = u.z; out[3] = u.w;
+  __device__ __forceinline__ static uint4 raw(const float* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static void widen(const uint4& u, float* out) {
+    out[0] = __uint_as_float(u.x); out[1] = __uint_as_float(u.y);
+    out[2] = __uint_as_float(u.z); out[3] = __uint_as_float(u.w);
   }
+  __device__ __forceinline__ static void load(const float* p, float* out) { widen(raw(p), out); }
 };
 
 // ---------------------------------------------------------------------------

@@ -42,21 +42,17 @@ __global__ __launch_bounds__(kPoolThreads) void pool_leaf_kernel(Geo g, const T*
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
     for (int r = r0 + rsub; r < r1; r += RPI * kUnroll) {
-      float x[kUnroll][VEC];
+      uint4 raw[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)  // unconditional loads from clamped rows, all in flight
+        raw[u] = Wide<T>::raw(kb + (int64_t)min(r + u * RPI, r1 - 1) * D + col);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const int row = r + u * RPI;
-        if (row < r1) {
-          Wide<T>::load(kb + (int64_t)row * D + col, x[u]);
-        } else {
+        float x[VEC];
+        Wide<T>::widen(raw[u], x);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) x[u][e] = 0.f;
-        }
+        for (int e = 0; e < VEC; ++e) acc[e] += r + u * RPI < r1 ? (double)x[e] : 0.0;
       }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += (double)x[u][e];
     }
     // sum the row slots that share these columns
 #pragma unroll

@@ -2,13 +2,12 @@
 // sans matrice de scores", section "La sélection top-K guidée par la
 // pyramide"): prune hard at the top level, refine one level at a time.
 //
-// One workgroup per (batch, kv head, query block). It first streams the query
+// One wave per (batch, kv head, query block). It first streams the query
 // block's rows of all heads in the KV group (the HBM-heavy part) into an fp64
 // mean, then descends the pyramid: each level scores its candidate pool with
-// fp64 dot products (16 lanes per node, one 512-byte summary row per lane
-// group), keeps the K best with a bitonic sort in LDS ordered by (score
-// descending, index ascending), and expands the kept nodes' children plus the
-// complete children of the query block's own ancestor.
+// fp64 dot products, keeps the K best (score descending, index ascending), and
+// expands the kept nodes' children plus the complete children of the query
+// block's own ancestor.
 //
 // The same descent serves decode, where the "block" is one query token.
 #include "pisa_internal.h"
@@ -17,16 +16,14 @@
 namespace pisa {
 namespace {
 
-// Mean of the query block's rows over the group's heads, into qbar (LDS, fp64).
+// Mean of the query block's rows over the group's heads (fp64), by one wave.
 template <typename T, int D>
-__device__ void block_query_mean(const Geo& g, const T* __restrict__ q, int b, int kvh, int qb, double* qbar,
-                                 double (*red)[D]) {
+__device__ __forceinline__ void wave_query_mean(const Geo& g, const T* __restrict__ q, int b, int kvh, int qb,
+                                                double* qbar, int lane) {
   constexpr int VEC = Wide<T>::kVec;
-  constexpr int LPR = D / VEC;
-  constexpr int RPI = 64 / LPR;
-  constexpr int kUnroll = 8;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  constexpr int LPR = D / VEC;   // lanes covering one row
+  constexpr int RPI = 64 / LPR;  // rows per wave instruction
+  constexpr int U = 16;          // loads in flight per lane
   const int col = (lane % LPR) * VEC;
   const int rsub = lane / LPR;
   const int r0 = qb * g.bs;
@@ -35,24 +32,22 @@ __device__ void block_query_mean(const Geo& g, const T* __restrict__ q, int b, i
   double acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
-  for (int t = wave * RPI + rsub; t < total; t += kSelectThreads / 64 * RPI * kUnroll) {
-    float x[kUnroll][VEC];
+  for (int t = rsub; t < total; t += RPI * U) {
+    uint4 raw[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int tt = t + u * (kSelectThreads / 64) * RPI;
-      if (tt < total) {
-        const int h = kvh * g.G + tt / rows;
-        const int r = r0 + tt % rows;
-        Wide<T>::load(q + (((int64_t)b * g.Hq + h) * g.N + r) * D + col, x[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) x[u][e] = 0.f;
-      }
+    for (int u = 0; u < U; ++u) {
+      // unconditional loads from a clamped (head, row) keep all of them in flight
+      const int tt = min(t + u * RPI, total - 1);
+      const int h = kvh * g.G + tt / rows;
+      raw[u] = Wide<T>::raw(q + (((int64_t)b * g.Hq + h) * g.N + r0 + tt % rows) * D + col);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < U; ++u) {
+      float x[VEC];
+      Wide<T>::widen(raw[u], x);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += (double)x[u][e];
+      for (int e = 0; e < VEC; ++e) acc[e] += t + u * RPI < total ? (double)x[e] : 0.0;
+    }
   }
 #pragma unroll
   for (int s = LPR; s < 64; s <<= 1)
@@ -60,40 +55,50 @@ __device__ void block_query_mean(const Geo& g, const T* __restrict__ q, int b, i
     for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], s);
   if (rsub == 0) {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) red[wave][col + e] = acc[e];
+    for (int e = 0; e < VEC; ++e) qbar[col + e] = acc[e] / (double)total;
   }
-  __syncthreads();
-  for (int c = threadIdx.x; c < D; c += kSelectThreads) {
-    double s = 0.0;
-#pragma unroll
-    for (int w = 0; w < kSelectThreads / 64; ++w) s += red[w][c];
-    qbar[c] = s / (double)total;
-  }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
 }
 
-template <typename T, int D>
+// One wave per (batch, kv head, query block); four per workgroup.
+template <typename T, int D, int E>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geo g, const T* __restrict__ q,
                                                                 const float* __restrict__ pyr,
-                                                                int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
-  __shared__ double qbar[D];
-  __shared__ double red[kSelectThreads / 64][D];
-  __shared__ DescentSmem sm;
-  const int qb = blockIdx.x;
-  const int slab = blockIdx.y;
-  const int b = slab / g.Hkv;
-  const int kvh = slab % g.Hkv;
-  block_query_mean<T, D>(g, q, b, kvh, qb, qbar, red);
-  const float* ps = pyr + (int64_t)slab * g.off[g.L] * D;
-  const int64_t unit = (int64_t)slab * g.nb + qb;
-  descend<D>(g, ps, qbar, qb, idx + unit * g.K, cnt + unit, sm);
+                                                                int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
+                                                                int units) {
+  __shared__ WaveSmem<E, D> smem[kSelectWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int u = blockIdx.x * kSelectWaves + wave;
+  if (u >= units) return;
+  const int slab = u / g.nb;
+  const int qb = u % g.nb;
+  if (g.K == 0) {
+    if (lane == 0) cnt[u] = 0;
+    return;
+  }
+  wave_query_mean<T, D>(g, q, slab / g.Hkv, slab % g.Hkv, qb, smem[wave].qbar, lane);
+  wave_descend<E, D>(g, pyr + (int64_t)slab * g.off[g.L] * D, qb, idx + (int64_t)u * g.K, cnt + u, smem[wave], lane);
+}
+
+template <typename T, int D, int E>
+hipError_t launch_select_e(const Geo& g, const void* q, const float* pyr, int32_t* idx, int32_t* cnt, hipStream_t s) {
+  const int units = g.B * g.Hkv * g.nb;
+  const int blocks = (units + kSelectWaves - 1) / kSelectWaves;
+  hipLaunchKernelGGL((select_kernel<T, D, E>), dim3(blocks), dim3(kSelectThreads), 0, s, g, (const T*)q, pyr, idx, cnt,
+                     units);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_select_t(const Geo& g, const void* q, const float* pyr, int32_t* idx, int32_t* cnt, hipStream_t s) {
-  dim3 grid(g.nb, g.B * g.Hkv);
-  hipLaunchKernelGGL((select_kernel<T, D>), grid, dim3(kSelectThreads), 0, s, g, (const T*)q, pyr, idx, cnt);
-  return hipGetLastError();
+  switch (pool_slots_per_lane(g)) {
+    case 1: return launch_select_e<T, D, 1>(g, q, pyr, idx, cnt, s);
+    case 2: return launch_select_e<T, D, 2>(g, q, pyr, idx, cnt, s);
+    case 4: return launch_select_e<T, D, 4>(g, q, pyr, idx, cnt, s);
+    case 8: return launch_select_e<T, D, 8>(g, q, pyr, idx, cnt, s);
+    default: return launch_select_e<T, D, 16>(g, q, pyr, idx, cnt, s);
+  }
 }
 
 }  // namespace

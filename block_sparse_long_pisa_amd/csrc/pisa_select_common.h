@@ -1,5 +1,14 @@
 // Pyramid descent shared by prefill selection and decode selection
-// ("La sélection top-K guidée par la pyramide").
+// ("Attention clairsemée PISA : noyaux Triton sans matrice de scores", section
+// "La sélection top-K guidée par la pyramide").
+//
+// One wave descends for one query block (or decode token). The candidate pool
+// of a level lives in registers, E slots per lane (pool capacity 64*E); nodes
+// are scored by 16-lane groups with fp64 dot products against the query mean,
+// and the pool is ordered best-first -- score descending, node index ascending --
+// by a bitonic sort across lanes (shuffles) and slots (register swaps). No
+// workgroup barrier is involved, so waves of one workgroup never wait on each
+// other.
 #pragma once
 
 #include <limits.h>
@@ -9,135 +18,372 @@
 namespace pisa {
 
 constexpr int kSelectThreads = 256;
+constexpr int kSelectWaves = kSelectThreads / 64;
 
-struct DescentSmem {
-  double score[kPoolMax];
-  int id[kPoolMax];
-  int kept[kMaxTopK];
-  int n_pool;
-};
-
-// Scores of pool nodes sm.id[0, M) against the fp64 query mean: 16 lanes per
-// node, each lane reading D/16 contiguous floats of the node's summary row.
-template <int D>
-__device__ __forceinline__ void score_pool(const float* __restrict__ lvl, const double* qbar, int M, DescentSmem& sm) {
-  constexpr int DPL = D / 16;
-  const int grp = threadIdx.x >> 4;
-  const int sub = threadIdx.x & 15;
-  double qv[DPL];
-#pragma unroll
-  for (int e = 0; e < DPL; ++e) qv[e] = qbar[sub * DPL + e];
-  for (int base = 0; base < M; base += kSelectThreads / 16) {
-    const int i = base + grp;
-    double s = 0.0;
-    if (i < M) {
-      const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)sm.id[i] * D + sub * DPL);
-#pragma unroll
-      for (int e4 = 0; e4 < DPL / 4; ++e4) {
-        const float4 x = row[e4];
-        s += qv[e4 * 4 + 0] * (double)x.x;
-        s += qv[e4 * 4 + 1] * (double)x.y;
-        s += qv[e4 * 4 + 2] * (double)x.z;
-        s += qv[e4 * 4 + 3] * (double)x.w;
-      }
-    }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    s += __shfl_xor(s, 8);
-    if (sub == 0 && i < M) sm.score[i] = s;
-  }
+// Pool slots per lane (a power of two) covering the largest pool of any level:
+// the top level's nodes, or K kept nodes' children plus the ancestor's.
+inline int pool_slots_per_lane(const Geo& g) {
+  const int mmax = max(g.nodes[g.L - 1], g.K * g.f + g.f - 1);
+  int e = 1;
+  while (64 * e < mmax) e <<= 1;
+  return e;
 }
+
+// Per-wave LDS: scores staged from the scoring layout to the sort layout, the
+// nodes kept at the previous level, and the query mean.
+template <int E, int D>
+struct WaveSmem {
+  double sc[64 * E];
+  int kept[kMaxTopK];
+  int nkept;
+  double qbar[D];
+};
 
 __device__ __forceinline__ bool ranks_before(double sa, int ia, double sb, int ib) {
   return sa > sb || (sa == sb && ia < ib);
 }
 
-// Bitonic sort of (score, id) pairs [0, M) in LDS, best first; pads to a power of two.
-__device__ __forceinline__ void bitonic_best_first(DescentSmem& sm, int M) {
-  int P = 1;
-  while (P < M) P <<= 1;
-  for (int i = M + threadIdx.x; i < P; i += kSelectThreads) {
-    sm.score[i] = -__builtin_inf();
-    sm.id[i] = INT_MAX;
-  }
-  __syncthreads();
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = threadIdx.x; i < P; i += kSelectThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const double si = sm.score[i], sj = sm.score[ixj];
-          const int ii = sm.id[i], ij = sm.id[ixj];
-          const bool asc = (i & k) == 0;
-          const bool sw = asc ? ranks_before(sj, ij, si, ii) : ranks_before(si, ii, sj, ij);
-          if (sw) {
-            sm.score[i] = sj;
-            sm.score[ixj] = si;
-            sm.id[i] = ij;
-            sm.id[ixj] = ii;
-          }
-        }
+// The same order without short-circuit evaluation: both operands are always
+// evaluated, so loads feeding it are never made conditional.
+__device__ __forceinline__ int ranks_before_nb(double sa, int ia, double sb, int ib) {
+  return (int)(sa > sb) | ((int)(sa == sb) & (int)(ia < ib));
+}
+
+// Compare-exchange of slots e and e ^ JJ inside each lane (bitonic stride 64 * JJ).
+template <int E, int JJ>
+__device__ __forceinline__ void inlane_stage(double (&s)[E], int (&id)[E], int k, int P, int lane) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if ((e & JJ) == 0 && (e | JJ) * 64 < P) {
+      const int e2 = e | JJ;
+      const bool asc = ((e * 64 + lane) & k) == 0;
+      const bool lo_first = ranks_before_nb(s[e], id[e], s[e2], id[e2]);
+      if (lo_first != asc) {
+        const double ts = s[e];
+        const int ti = id[e];
+        s[e] = s[e2];
+        id[e] = id[e2];
+        s[e2] = ts;
+        id[e2] = ti;
       }
-      __syncthreads();
     }
   }
 }
 
-// Descent for query block (or decode token) qb of one (batch, kv head) slab.
-// ps: the slab's pyramid; qbar: fp64 query mean in LDS (already synchronised).
-// Writes out_idx[0, K) (ascending, -1 padded) and *out_cnt.
-template <int D>
-__device__ void descend(const Geo& g, const float* __restrict__ ps, const double* qbar, int qb,
-                        int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt, DescentSmem& sm) {
-  const int tid = threadIdx.x;
+// Bitonic sort, best first, of the first P (a power of two <= 64 * E) slots,
+// slot e of lane l holding position e * 64 + l.
+template <int E>
+__device__ __forceinline__ void wave_sort(double (&s)[E], int (&id)[E], int P, int lane) {
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        const int jj = j >> 6;
+        if constexpr (E >= 2) if (jj == 1) inlane_stage<E, 1>(s, id, k, P, lane);
+        if constexpr (E >= 4) if (jj == 2) inlane_stage<E, 2>(s, id, k, P, lane);
+        if constexpr (E >= 8) if (jj == 4) inlane_stage<E, 4>(s, id, k, P, lane);
+        if constexpr (E >= 16) if (jj == 8) inlane_stage<E, 8>(s, id, k, P, lane);
+      } else {
+        const bool lower = (lane & j) == 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if (e * 64 < P) {
+            const double os = __shfl_xor(s[e], j);
+            const int oi = __shfl_xor(id[e], j);
+            const bool asc = ((e * 64 + lane) & k) == 0;
+            const bool mine_first = ranks_before_nb(s[e], id[e], os, oi);
+            // the lower position of an ascending pair keeps the better element
+            if (mine_first != (lower == asc)) {
+              s[e] = os;
+              id[e] = oi;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// Node id held by pool slot p at level l (kept children first, then the
+// complete children of the query block's own ancestor).
+__device__ __forceinline__ int slot_node(int p, int nchild, int f, const int* kept, int anc_first) {
+  return p < nchild ? kept[p / f] * f + p % f : anc_first + (p - nchild);
+}
+
+// Score pool slots [0, M) into sm.sc (fp64 dot products with the query mean).
+// 16 lanes per node, four nodes per wave instruction, four instructions in flight.
+template <int E, int D, int NWS>
+__device__ __forceinline__ void score_slots(const float* __restrict__ lvl, int M, int nchild, int f, int anc_first,
+                                            int lo, WaveSmem<E, D>& sm, const double (&qv)[D / 16], int lane,
+                                            int wave) {
+  constexpr int DPL = D / 16;
+  constexpr int U = 8;
+  const int grp = wave * 4 + (lane >> 4);  // 16-lane group among the NWS cooperating waves
+  const int sub = lane & 15;
+  for (int base = 0; base < M; base += 4 * NWS * U) {
+    float4 x[U][DPL / 4];
+    bool use[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = base + u * 4 * NWS + grp;
+      const int n = p < M ? slot_node(p, nchild, f, sm.kept, anc_first) : 0;
+      use[u] = p < M && n >= lo;
+      // unused slots read node 0 (always present) so that no load is conditional
+      const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)(use[u] ? n : 0) * D + sub * DPL);
+#pragma unroll
+      for (int e4 = 0; e4 < DPL / 4; ++e4) x[u][e4] = row[e4];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      double acc = 0.0;
+#pragma unroll
+      for (int e4 = 0; e4 < DPL / 4; ++e4) {
+        acc += qv[e4 * 4 + 0] * (double)x[u][e4].x;
+        acc += qv[e4 * 4 + 1] * (double)x[u][e4].y;
+        acc += qv[e4 * 4 + 2] * (double)x[u][e4].z;
+        acc += qv[e4 * 4 + 3] * (double)x[u][e4].w;
+      }
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 4);
+      acc += __shfl_xor(acc, 8);
+      const int p = base + u * 4 * NWS + grp;
+      if (sub == 0 && p < M) sm.sc[p] = use[u] ? acc : -__builtin_inf();
+    }
+  }
+}
+
+// Descent of one wave for query block (or decode token) qb of one slab.
+// ps: the slab's pyramid; sm.qbar: the fp64 query mean (written by this wave).
+// Writes out_idx[0, K) ascending, -1 padded, and *out_cnt.
+// With NWS > 1 the NWS waves of a workgroup score each level's pool together
+// (more loads in flight when the pyramid is not cached) and wave 0 sorts.
+template <int NWS>
+__device__ __forceinline__ void sync_scorers() {
+  if constexpr (NWS > 1) __syncthreads();
+  else __builtin_amdgcn_wave_barrier();
+}
+
+// Descent of one wave for query block (or decode token) qb of one slab.
+// ps: the slab's pyramid; sm.qbar: the fp64 query mean (written by this wave).
+// Writes out_idx[0, K) ascending, -1 padded, and *out_cnt. A level whose valid
+// pool holds at most K nodes keeps them all, so it is not scored.
+template <int E, int D, int NWS = 1>
+__device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb, int32_t* __restrict__ out_idx,
+                             int32_t* __restrict__ out_cnt, WaveSmem<E, D>& sm, int lane, int wave = 0) {
+  constexpr int DPL = D / 16;
+  if (g.K == 0) {
+    if (lane == 0 && wave == 0) *out_cnt = 0;
+    return;
+  }
+  double qv[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) qv[e] = sm.qbar[(lane & 15) * DPL + e];
   const int L = g.L;
+  // top level: complete nodes before the ancestor that hold a non-sink block
+  int lo = g.j0 / g.span[L - 1];
+  int M = max(0, qb / g.span[L - 1] - lo);
+  int nchild = 0;      // slots that are children of kept nodes
+  int anc_first = lo;  // first node of the contiguous tail of the pool
+  for (int l = L - 1; l >= 0; --l) {
+    // slot ids and validity need no scores
+    int id[E];
+    int nvalid = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int p = e * 64 + lane;
+      const int n = p < M ? slot_node(p, nchild, g.f, sm.kept, anc_first) : INT_MAX;
+      const bool valid = p < M && n >= lo;
+      id[e] = valid ? n : INT_MAX;
+      nvalid += __popcll(__ballot(valid));
+    }
+    const int nk = min(g.K, nvalid);
+    const bool ranked = nvalid > g.K;  // uniform across the cooperating waves
+    if (ranked) {
+      score_slots<E, D, NWS>(ps + (int64_t)g.off[l] * D, M, nchild, g.f, anc_first, lo, sm, qv, lane, wave);
+      sync_scorers<NWS>();
+    }
+    if (NWS > 1 && wave != 0) {  // helpers: wait for wave 0's kept list, then go on
+      if (l == 0) return;
+      sync_scorers<NWS>();
+      const int a_l = qb / g.span[l];
+      nchild = nk * g.f;
+      anc_first = a_l * g.f;
+      M = nchild + (qb / g.span[l - 1] - anc_first);
+      lo = g.j0 / g.span[l - 1];
+      continue;
+    }
+    if (ranked) {
+      double s[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int p = e * 64 + lane;
+        s[e] = (p < M && id[e] != INT_MAX) ? sm.sc[p] : -__builtin_inf();
+      }
+      int P = 64;
+      while (P < M) P <<= 1;
+      wave_sort<E>(s, id, P, lane);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (e * 64 + lane < nk) sm.kept[e * 64 + lane] = id[e];
+    } else {
+      // keep every valid slot, compacted in slot order
+      int base = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const unsigned long long m = __ballot(id[e] != INT_MAX);
+        if (id[e] != INT_MAX) sm.kept[base + __popcll(m & ((1ull << lane) - 1))] = id[e];
+        base += __popcll(m);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (l == 0) {
+      for (int t = lane; t < nk; t += 64) {
+        const int v = sm.kept[t];
+        int r = 0;
+        for (int u = 0; u < nk; ++u) r += (sm.kept[u] < v);
+        out_idx[r] = v;
+      }
+      for (int t = nk + lane; t < g.K; t += 64) out_idx[t] = -1;
+      if (lane == 0) *out_cnt = nk;
+      return;
+    }
+    sync_scorers<NWS>();
+    // next level's pool: children of the kept nodes, then the complete children
+    // of the ancestor; nodes wholly inside the sink are invalid
+    const int a_l = qb / g.span[l];
+    nchild = nk * g.f;
+    anc_first = a_l * g.f;
+    M = nchild + (qb / g.span[l - 1] - anc_first);
+    lo = g.j0 / g.span[l - 1];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Descent by a whole workgroup of NT threads for one query (decode): each level's
+// pool is scored in one round of loads (U nodes per 16-lane group), and each
+// candidate's place in the best-first order is its count of candidates that
+// rank before it, so no sort is needed.
+
+struct BlockSmem {
+  double sc[kPoolMax + 8];
+  int id[kPoolMax + 8];
+  int kept[kMaxTopK];
+  int nvalid;
+};
+
+template <int D, int NT, int U>
+__device__ void block_descend(const Geo& g, const float* __restrict__ ps, int qb, const double* qbar,
+                              int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt, BlockSmem& sm) {
+  constexpr int DPL = D / 16;
+  constexpr int NG = NT / 16;  // 16-lane groups
+  const int tid = threadIdx.x;
+  const int grp = tid >> 4;
+  const int sub = tid & 15;
   if (g.K == 0) {
     if (tid == 0) *out_cnt = 0;
     return;
   }
-  {
-    const int lo = g.j0 / g.span[L - 1];
-    const int hi = qb / g.span[L - 1];
-    const int n = max(0, hi - lo);
-    for (int i = tid; i < n; i += kSelectThreads) sm.id[i] = lo + i;
-    if (tid == 0) sm.n_pool = n;
-  }
-  __syncthreads();
+  double qv[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) qv[e] = qbar[sub * DPL + e];
+  const int L = g.L;
+  int lo = g.j0 / g.span[L - 1];
+  int M = max(0, qb / g.span[L - 1] - lo);
+  int nchild = 0, anc_first = lo;
   for (int l = L - 1; l >= 0; --l) {
-    const int M = sm.n_pool;
-    score_pool<D>(ps + (int64_t)g.off[l] * D, qbar, M, sm);
+    const float* lvl = ps + (int64_t)g.off[l] * D;
+    // valid slots need no scores; a level with at most K of them keeps them all
+    int nv_local = 0;
+    for (int p = tid; p < M; p += NT) nv_local += slot_node(p, nchild, g.f, sm.kept, anc_first) >= lo ? 1 : 0;
+    if (tid == 0) sm.nvalid = 0;
     __syncthreads();
-    int nk = M;
-    if (M > g.K) {
-      bitonic_best_first(sm, M);
-      nk = g.K;
+    if (nv_local) atomicAdd(&sm.nvalid, nv_local);
+    __syncthreads();
+    const int nvalid = sm.nvalid;
+    const bool ranked = nvalid > g.K;
+    for (int base = 0; ranked && base < M; base += NG * U) {
+      float4 x[U][DPL / 4];
+      int node[U];
+      bool use[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = base + u * NG + grp;
+        node[u] = p < M ? slot_node(p, nchild, g.f, sm.kept, anc_first) : 0;
+        use[u] = p < M && node[u] >= lo;
+        const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)(use[u] ? node[u] : 0) * D + sub * DPL);
+#pragma unroll
+        for (int e4 = 0; e4 < DPL / 4; ++e4) x[u][e4] = row[e4];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        double acc = 0.0;
+#pragma unroll
+        for (int e4 = 0; e4 < DPL / 4; ++e4) {
+          acc += qv[e4 * 4 + 0] * (double)x[u][e4].x;
+          acc += qv[e4 * 4 + 1] * (double)x[u][e4].y;
+          acc += qv[e4 * 4 + 2] * (double)x[u][e4].z;
+          acc += qv[e4 * 4 + 3] * (double)x[u][e4].w;
+        }
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        acc += __shfl_xor(acc, 4);
+        acc += __shfl_xor(acc, 8);
+        const int p = base + u * NG + grp;
+        if (sub == 0 && p < M) {
+          sm.sc[p] = use[u] ? acc : -__builtin_inf();
+          sm.id[p] = use[u] ? node[u] : INT_MAX;
+        }
+      }
     }
+    // sentinels up to a multiple of 8 never rank before a candidate
+    if (ranked && tid < 8 && M + tid < ((M + 7) & ~7)) {
+      sm.sc[M + tid] = -__builtin_inf();
+      sm.id[M + tid] = INT_MAX;
+    }
+    __syncthreads();
+    const int nk = min(g.K, nvalid);
+    if (!ranked) {  // keep every valid slot in slot order (few: at most K)
+      if (tid == 0) {
+        int c = 0;
+        for (int p = 0; p < M; ++p) {
+          const int n = slot_node(p, nchild, g.f, sm.kept, anc_first);
+          if (n >= lo) sm.id[c++] = n;
+        }
+        for (int t = 0; t < c; ++t) sm.kept[t] = sm.id[t];
+      }
+    } else
+    for (int p = tid; p < M; p += NT) {
+      const int myid = sm.id[p];
+      const double mys = sm.sc[p];
+      int r = 0;
+      // branch-free: eight independent broadcast reads per step (padded with sentinels)
+      const double* sp = sm.sc;
+      const int* ip = sm.id;
+      for (int q0 = 0; q0 < M; q0 += 8, sp += 8, ip += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r += ranks_before_nb(sp[u], ip[u], mys, myid);
+      }
+      if (myid != INT_MAX && r < nk) sm.kept[r] = myid;
+    }
+    __syncthreads();
     if (l == 0) {
-      for (int t = tid; t < nk; t += kSelectThreads) {
-        const int v = sm.id[t];
+      for (int t = tid; t < nk; t += NT) {
+        const int v = sm.kept[t];
         int r = 0;
-        for (int u = 0; u < nk; ++u) r += (sm.id[u] < v);
+        for (int u = 0; u < nk; ++u) r += (sm.kept[u] < v);
         out_idx[r] = v;
       }
-      for (int t = nk + tid; t < g.K; t += kSelectThreads) out_idx[t] = -1;
+      for (int t = nk + tid; t < g.K; t += NT) out_idx[t] = -1;
       if (tid == 0) *out_cnt = nk;
       return;
     }
-    for (int t = tid; t < nk; t += kSelectThreads) sm.kept[t] = sm.id[t];
-    __syncthreads();
-    if (tid == 0) sm.n_pool = 0;
-    __syncthreads();
-    const int lo = g.j0 / g.span[l - 1];
     const int a_l = qb / g.span[l];
     const int a_below = qb / g.span[l - 1];
-    const int nchild = nk * g.f;
-    const int nanc = a_below - a_l * g.f;  // complete children of qb's own ancestor
-    for (int t = tid; t < nchild + nanc; t += kSelectThreads) {
-      const int c = t < nchild ? sm.kept[t / g.f] * g.f + t % g.f : a_l * g.f + (t - nchild);
-      if (c >= lo) sm.id[atomicAdd(&sm.n_pool, 1)] = c;
-    }
-    __syncthreads();
+    nchild = nk * g.f;
+    anc_first = a_l * g.f;
+    M = nchild + (a_below - anc_first);
+    lo = g.j0 / g.span[l - 1];
   }
 }
 
