@@ -74,35 +74,80 @@ __device__ __forceinline__ TileWalk make_walk(const Geo& g, int qb, const int* s
   return w;
 }
 
-// LDS tiles hold key rows of D bf16 as 16-byte chunks; chunk cc of row r sits at
-// chunk position cc ^ swz(r). The swizzle keeps the two read patterns free of
-// bank conflicts: 16 consecutive rows at one chunk (K fragments of S^T = K Q^T)
-// and 4 consecutive rows x 4 consecutive chunks (transposing V^T reads).
-template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
-}
+// LDS tiles hold key rows with padded pitches chosen so that both read
+// patterns are free of bank conflicts: K rows are D + 8 bf16 apart (16
+// consecutive rows at one 16-byte chunk land on distinct banks), V rows D + 32
+// apart (4 consecutive rows x 64 bytes, the transposing V^T reads, cover all
+// banks once). Every read is then a per-lane base register plus an immediate.
+template <int D, int BS = 128>
+struct TilePitch {
+  static constexpr int K = D + 8;   // bf16 elements per K row
+  static constexpr int V = D + 32;  // bf16 elements per V row
+  static constexpr int KU = K / 8;  // 16-byte units per K row
+  static constexpr int VU = V / 8;
+  // whole 1 KB wave copies per tile; the LDS arrays are sized to match
+  static constexpr int KI = (BS * KU + 63) / 64;
+  static constexpr int VI = (BS * VU + 63) / 64;
+  static constexpr int KSIZE = KI * 512;  // bf16 elements
+  static constexpr int VSIZE = VI * 512;
+};
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
 
+// Source offset (elements) within a tile of the 16-byte unit u of a padded LDS
+// tile; padding units (and the slack past the tile) re-read the row's first
+// chunk, rows past `rows` re-read the last valid row (their keys are masked).
+template <int D, int UPR>
+__device__ __forceinline__ int unit_src(int u, int rows) {
+  const int r = u / UPR, cu = u % UPR;
+  return min(r, rows - 1) * D + (cu < D / 8 ? cu : 0) * 8;
+}
+
+// Per-lane source offsets of this wave's copies of a full tile (they do not
+// change from tile to tile).
+template <int D, int BS, int NW>
+struct DmaPlan {
+  using TP = TilePitch<D, BS>;
+  static constexpr int KN = (TP::KI + NW - 1) / NW;
+  static constexpr int VN = (TP::VI + NW - 1) / NW;
+  int k[KN];
+  int v[VN];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int n = 0; n < KN; ++n) k[n] = unit_src<D, TP::KU>((wave + NW * n) * 64 + lane, BS);
+#pragma unroll
+    for (int n = 0; n < VN; ++n) v[n] = unit_src<D, TP::VU>((wave + NW * n) * 64 + lane, BS);
+  }
+};
+
 // Issue the asynchronous global->LDS copies of one K and one V tile (block j).
-// Each wave instruction fills 64 consecutive 16-byte LDS chunks; rows past the
-// end of the sequence re-read the last valid row (their keys are masked).
+// Each wave instruction fills 64 consecutive 16-byte LDS units in row order.
 template <int D, int BS, int NW>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
-                                           int rows_in_mem, uint16_t* kdst, uint16_t* vdst, int wave, int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int INSTR = BS * CPR / 64;
-  for (int i = wave; i < INSTR; i += NW) {
-    const int u = i * 64 + lane;
-    const int r = u / CPR;
-    const int cc = (u % CPR) ^ swz<CPR>(r);
-    const int gr = min(r, rows_in_mem - 1);
-    __builtin_amdgcn_global_load_lds(kt + gr * D + cc * 8, (lds_void_ptr)(kdst + i * 512), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vt + gr * D + cc * 8, (lds_void_ptr)(vdst + i * 512), 16, 0, 0);
+                                           int rows_in_mem, uint16_t* kdst, uint16_t* vdst, int wave, int lane,
+                                           const DmaPlan<D, BS, NW>& plan) {
+  using TP = TilePitch<D, BS>;
+  using PL = DmaPlan<D, BS, NW>;
+  // a planned offset row * D + col keeps its column; rows past the last valid
+  // one (only in a sequence's ragged last block) move to the last valid row
+  const int last = (rows_in_mem - 1) * D;
+#pragma unroll
+  for (int n = 0; n < PL::KN; ++n) {
+    const int i = wave + NW * n;
+    if (i < TP::KI) {
+      const int off = min(plan.k[n], last + (plan.k[n] & (D - 1)));
+      __builtin_amdgcn_global_load_lds(kt + off, (lds_void_ptr)(kdst + i * 512), 16, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < PL::VN; ++n) {
+    const int i = wave + NW * n;
+    if (i < TP::VI) {
+      const int off = min(plan.v[n], last + (plan.v[n] & (D - 1)));
+      __builtin_amdgcn_global_load_lds(vt + off, (lds_void_ptr)(vdst + i * 512), 16, 0, 0);
+    }
   }
 }
 
@@ -119,15 +164,15 @@ struct AttnState {
   bf16x8_t qf[NDS];
   f32x16_t oacc[NDB];
   float m_run, l_run;
-  int offk[NDS];      // byte offsets of this lane's K-fragment chunks
-  int offv[2][NDB];   // byte offsets of this lane's V^T transposing reads
+  int offk;      // byte offset of this lane's first K-fragment chunk in a K tile
+  int offv;      // byte offset of this lane's first V^T transposing read in a V tile
 };
 
 // One key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T, in chunks of
 // at most 64 keys (32 live accumulator registers for S per chunk).
 template <int D, int BS>
 __device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_t* ks, const uint16_t* vs, int nvalid,
-                                             bool local, int key0, int qpos, int hi, float c) {
+                                             bool local, int key0, int qpos, int hi, float c, int wg_qmax) {
   constexpr int CPR = D / 8;
   constexpr int NDS = D / 16, NDB = D / 32;
   constexpr int KC = BS < 64 ? BS : 64;  // keys per chunk
@@ -136,6 +181,9 @@ __device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_
   const char* vb_base = reinterpret_cast<const char*>(vs);
 #pragma unroll
   for (int ch = 0; ch < BS / KC; ++ch) {
+    // a chunk past the valid keys, or wholly after the workgroup's last query on
+    // the causal diagonal, contributes nothing to any row (uniform test)
+    if (ch > 0 && (ch * KC >= nvalid || (local && key0 + ch * KC > wg_qmax))) break;
     f32x16_t sacc[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -143,8 +191,8 @@ __device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_
       for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(kb_base + st.offk[ds] + (ch * KC + kb * 32) * CPR * 16);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb_base + st.offk + ds * 32 +
+                                                              (ch * KC + kb * 32) * TilePitch<D>::K * 2);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[ds], sacc[kb], 0, 0, 0);
       }
     }
@@ -198,13 +246,13 @@ __device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_
         bf16x8_t pb;
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][hh * 8 + e];
-        const int step = (ch * KC + kb * 32 + hh * 16) * CPR * 16;
+        const int step = (ch * KC + kb * 32 + hh * 16) * TilePitch<D>::V * 2;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const v4i16_t lo =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vb_base + st.offv[0][db] + step));
-          const v4i16_t up =
-              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vb_base + st.offv[1][db] + step));
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_ptr)(vb_base + st.offv + step + db * 64));
+          const v4i16_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_v4i16_ptr)(vb_base + st.offv + step + db * 64 + 8 * TilePitch<D>::V * 2));
           const v4i16_t a8[2] = {lo, up};
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a8);
           st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, st.oacc[db], 0, 0, 0);
@@ -226,10 +274,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
   constexpr int NDS = D / 16;
   constexpr int NDB = D / 32;
   // two stages of K and V tiles, filled by asynchronous copies
-  __shared__ __attribute__((aligned(16))) uint16_t K0[BS * D];
-  __shared__ __attribute__((aligned(16))) uint16_t V0[BS * D];
-  __shared__ __attribute__((aligned(16))) uint16_t K1[BS * D];
-  __shared__ __attribute__((aligned(16))) uint16_t V1[BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t K0[TilePitch<D, BS>::KSIZE];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[TilePitch<D, BS>::VSIZE];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[TilePitch<D, BS>::KSIZE];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[TilePitch<D, BS>::VSIZE];
   __shared__ int sel[kMaxTopK];
 
   // heaviest units first; consecutive workgroups walk the (batch, kv head) slabs
@@ -242,7 +290,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
   const int b = slab / g.Hkv;
   const int kvh = slab % g.Hkv;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep it scalar
   const int l32 = lane & 31;
   const int hi = lane >> 5;
   const int pair = part * NW + wave;
@@ -270,31 +318,27 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
     for (int i = 0; i < 16; ++i) st.oacc[db][i] = 0.f;
   st.m_run = -__builtin_inff();
   st.l_run = 0.f;
-  {
-    const int gk = swz<CPR>(l32);
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) st.offk[ds] = (l32 * CPR + ((2 * ds + hi) ^ gk)) * 16;
-    const int cl = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-    for (int sec = 0; sec < 2; ++sec) {
-      const int rr = hi * 4 + ((lane & 15) >> 2) + 8 * sec;
-      const int x = cl ^ swz<CPR>(rr);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) st.offv[sec][db] = (rr * CPR + ((4 * db) ^ x)) * 16 + (lane & 1) * 8;
-    }
-  }
+  // K fragment: row l32, d = ds*16 + hi*8. V^T transposing read: lanes 4j..4j+3 of
+  // each 16-lane block supply row j's four 8-byte pieces of a 16-column slice.
+  st.offk = (l32 * TilePitch<D>::K + hi * 8) * 2;
+  st.offv = ((hi * 4 + ((lane & 15) >> 2)) * TilePitch<D>::V + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
   const float c = g.scale * kLog2e;
+  // last query position any wave of this workgroup holds (chunks of keys beyond
+  // it are masked for every row and are skipped)
+  const int wg_qmax = qb * BS + (((part + 1) * NW - 1) / g.G) * 32 + 31;
 
   const uint16_t* kbase = k + ((int64_t)b * g.Hkv + kvh) * g.N * D;
   const uint16_t* vbase = v + ((int64_t)b * g.Hkv + kvh) * g.N * D;
   __syncthreads();
   const TileWalk walk = make_walk(g, qb, sel, nsel);
+  DmaPlan<D, BS, NW> plan;
+  plan.init(wave, lane);
 
   int j, nvalid;
   bool local;
   walk.at(0, sel, g, qb, local_rows, j, nvalid, local);
   issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
-                        wave, lane);
+                        wave, lane, plan);
   for (int t = 0; t < walk.ntiles; t += 2) {
     // even tile: compute from stage 0 while stage 1 fills
     wait_loads_and_sync();
@@ -303,18 +347,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
     if (t + 1 < walk.ntiles) {
       walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
       issue_tile<D, BS, NW>(kbase + (int64_t)j1 * BS * D, vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K1,
-                            V1, wave, lane);
+                            V1, wave, lane, plan);
     }
-    compute_tile<D, BS>(st, K0, V0, nvalid, local, j * BS, qpos, hi, c);
+    compute_tile<D, BS>(st, K0, V0, nvalid, local, j * BS, qpos, hi, c, wg_qmax);
     if (t + 1 >= walk.ntiles) break;
     // odd tile: compute from stage 1 while stage 0 fills
     wait_loads_and_sync();
     if (t + 2 < walk.ntiles) {
       walk.at(t + 2, sel, g, qb, local_rows, j, nvalid, local);
       issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
-                            wave, lane);
+                            wave, lane, plan);
     }
-    compute_tile<D, BS>(st, K1, V1, nv1, loc1, j1 * BS, qpos, hi, c);
+    compute_tile<D, BS>(st, K1, V1, nv1, loc1, j1 * BS, qpos, hi, c, wg_qmax);
   }
 
   if (qvalid) {
