@@ -26,6 +26,38 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12  # B/s, MI355X
 BF16_PEAK = 2.5e15  # flop/s, dense bf16 matrix cores
 
+# HBM traffic per launch on these two workloads, from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch). Each counter is scaled by what
+# it reads for a plain device copy of 1 GiB into 1 GiB: FETCH_SIZE reports
+# 524334.9 KiB for the copy's 1 GiB of reads, WRITE_SIZE 1048576 KiB for its
+# writes. A figure holds only for the kernel source it was taken on: the sources
+# are hashed at run time and a changed kernel reports null.
+COPY_SCALE = {"fetch": 1048576.0 / 524334.9, "write": 1048576.0 / 1048576.0}
+MEASURED_TRAFFIC = {
+    # step: (sources, sha256 prefix of their bytes in this order, FETCH_SIZE KiB, WRITE_SIZE KiB)
+    "attention": (("pisa_attn.hip", "pisa_internal.h"), "3f68bdf1fb3a17ee", 5680215.2, 1048576.0),
+    "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "9cf176bad1868934",
+                131118.2 + 265.5 + 41.5, 4608.5 + 64.0 + 8.0),  # leaf + two coarse levels
+    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "c7c2421cf7f284f2",
+               552424.7, 1110.0),
+    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h"), "c90bfc6f962a28c9",
+               50355.5 + 551148.7 + 5393.0, 80.0 + 9504.0 + 512.0),  # select + split attention + merge
+}
+
+
+def measured_traffic(step):
+    """Scaled HBM bytes (read + written) of one launch of `step`, or None if its kernel changed since."""
+    import hashlib
+
+    files, digest, fetch_kib, write_kib = MEASURED_TRAFFIC[step]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "block_sparse_long_pisa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if not h.hexdigest().startswith(digest):
+        return None
+    return round(1024.0 * (fetch_kib * COPY_SCALE["fetch"] + write_kib * COPY_SCALE["write"]))
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -254,17 +286,17 @@ def run_prefill(args, dev):
             "peak": BF16_PEAK / 1e12,
             "unit": "TFLOP/s",
             "frac": flops / t_att / BF16_PEAK,
-            "traffic": None,
+            "traffic": measured_traffic("attention"),
             "algorithmic_flops_per_launch": flops,
             "avg_launch_ms": t_att * 1e3,
         },
         "kernels": {
             "pyramid": {"ms": t_pool * 1e3, "bound": "hbm", "bytes": b_pool, "GB/s": b_pool / t_pool / 1e9,
-                        "frac": b_pool / t_pool / HBM_PEAK},
+                        "frac": b_pool / t_pool / HBM_PEAK, "traffic": measured_traffic("pyramid")},
             "select": {"ms": t_sel * 1e3, "bound": "hbm", "bytes": b_sel, "GB/s": b_sel / t_sel / 1e9,
-                       "frac": b_sel / t_sel / HBM_PEAK},
+                       "frac": b_sel / t_sel / HBM_PEAK, "traffic": measured_traffic("select")},
             "attention": {"ms": t_att * 1e3, "bound": "mfma", "flops": flops, "TFLOP/s": flops / t_att / 1e12,
-                          "frac": flops / t_att / BF16_PEAK, "attended_pairs": pairs},
+                          "frac": flops / t_att / BF16_PEAK, "attended_pairs": pairs, "traffic": measured_traffic("attention")},
         },
     }
 
@@ -329,6 +361,7 @@ def run_decode(args, dev):
         "bytes_per_step": db,
         "GB/s": db / t_dec_ev / 1e9,
         "frac": db / t_dec_ev / HBM_PEAK,
+        "traffic": measured_traffic("decode"),
     }
     return decode
 

@@ -155,3 +155,30 @@ def test_decode_workspace_reuse_and_errors():
     assert torch.equal(a, b)
     with pytest.raises(pisa.PisaError):
         pisa.decode_step(cp, qd, kd, vd, pyr, 1024, workspace=ws[:16])
+
+
+def _golden():
+    import json
+    import os
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _golden()["descents"], ids=lambda c: c["name"])
+def test_hand_worked_descents_on_gpu(case):
+    """The hand-worked descents, embedded in the first of 64 dimensions with 32-token blocks."""
+    bs, d = 32, 64
+    means = np.asarray(case["block_means"], np.float32)
+    N = len(means) * bs
+    p = P(1, 1, 1, N, d, bs, case["fanout"], case["levels"], case["top_k"], case["sink_blocks"] * bs, "f32")
+    log(f"case hand-worked {case['name']}: {p}")
+    k = np.zeros((1, 1, N, d), np.float32)
+    k[0, 0, :, 0] = np.repeat(means, bs)
+    q = np.zeros((1, 1, N, d), np.float32)
+    q[0, 0, :, 0] = case["qbar"]
+    v = np.zeros_like(k)
+    levels, gi, gc, _, _ = gpu_prefill(p, to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32"), want_lse=False)
+    qb = case["query_block"]
+    assert gi[0, 0, qb, :gc[0, 0, qb]].tolist() == case["selected"]
+    assert np.all(gi[0, 0, qb, gc[0, 0, qb]:] == -1)
