@@ -34,6 +34,18 @@ constexpr float kLn2 = 0.6931471805599453f;
 // below 2^-126 only ever weigh a softmax term that is negligible anyway.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions across the two half-waves (lanes l and l ^ 32): v_permlane32_swap
+// exchanges one half of its first operand with the other half of its second, so
+// with x in both operands the two results hold x of both halves in every lane.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Which key block a tile index refers to, and how many of its keys count.
 struct TileWalk {
   int nfull_sink;    // blocks wholly inside the sink (before qb)
@@ -212,7 +224,7 @@ __device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_halves(mx);
     const float mt = mx * c;
     const bool move = mt > st.m_run + 8.f;
     const float m_ref = move ? mt : st.m_run;
@@ -235,8 +247,6 @@ __device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_
         sacc[kb][i] = p;
         rs += p;
       }
-    rs += __shfl_xor(rs, 32);
-    st.l_run += rs;
     // O^T[d][query] += V^T P^T over 16-key steps; slot (hi, e) of step (kb, hh)
     // holds key kb*32 + hh*16 + (e/4)*8 + hi*4 + e%4
 #pragma unroll
@@ -259,6 +269,7 @@ __device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_
         }
       }
     }
+    st.l_run += sum_halves(rs);
   }
 }
 

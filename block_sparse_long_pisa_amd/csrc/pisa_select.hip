@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geo g, const T* 
                                                                 int units) {
   __shared__ WaveSmem<E, D> smem[kSelectWaves];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep the descent scalar
   const int u = blockIdx.x * kSelectWaves + wave;
   if (u >= units) return;
   const int slab = u / g.nb;

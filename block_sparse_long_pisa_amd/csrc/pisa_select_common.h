@@ -5,8 +5,8 @@
 // One wave descends for one query block (or decode token). The candidate pool
 // of a level lives in registers, E slots per lane (pool capacity 64*E); nodes
 // are scored by 16-lane groups with fp64 dot products against the query mean,
-// and the pool is ordered best-first -- score descending, node index ascending --
-// by a bitonic sort across lanes (shuffles) and slots (register swaps). No
+// and the best K -- score descending, node index ascending -- are found by a
+// bitwise search for the K-th largest score with wave-wide counts, no sort. No
 // workgroup barrier is involved, so waves of one workgroup never wait on each
 // other.
 #pragma once
@@ -49,57 +49,59 @@ __device__ __forceinline__ int ranks_before_nb(double sa, int ia, double sb, int
   return (int)(sa > sb) | ((int)(sa == sb) & (int)(ia < ib));
 }
 
-// Compare-exchange of slots e and e ^ JJ inside each lane (bitonic stride 64 * JJ).
-template <int E, int JJ>
-__device__ __forceinline__ void inlane_stage(double (&s)[E], int (&id)[E], int k, int P, int lane) {
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    if ((e & JJ) == 0 && (e | JJ) * 64 < P) {
-      const int e2 = e | JJ;
-      const bool asc = ((e * 64 + lane) & k) == 0;
-      const bool lo_first = ranks_before_nb(s[e], id[e], s[e2], id[e2]);
-      if (lo_first != asc) {
-        const double ts = s[e];
-        const int ti = id[e];
-        s[e] = s[e2];
-        id[e] = id[e2];
-        s[e2] = ts;
-        id[e2] = ti;
-      }
-    }
-  }
+// Order-preserving map of an fp64 score to an unsigned key (larger score,
+// larger key); -0.0 counts as +0.0, as equal scores must tie.
+__device__ __forceinline__ uint64_t score_key(double s) {
+  const uint64_t u = (uint64_t)__double_as_longlong(s + 0.0);
+  return (u >> 63) ? ~u : (u | (1ull << 63));
 }
 
-// Bitonic sort, best first, of the first P (a power of two <= 64 * E) slots,
-// slot e of lane l holding position e * 64 + l.
+// Keep the nk best of the wave's pool slots -- score descending, node index
+// ascending -- without sorting. key[e] is 0 for an empty slot, so only valid
+// slots (nk <= their count) are ever kept. The nk-th largest key T is found bit
+// by bit with wave-wide counts; every slot above T is kept, and of the slots at
+// T the lowest node indices fill the rest. Writes the kept node ids to kept[]
+// in slot order. All slots take part in every count (empty ones never reach a
+// threshold), so the counts stay scalar and branch-free.
 template <int E>
-__device__ __forceinline__ void wave_sort(double (&s)[E], int (&id)[E], int P, int lane) {
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j >= 64) {
-        const int jj = j >> 6;
-        if constexpr (E >= 2) if (jj == 1) inlane_stage<E, 1>(s, id, k, P, lane);
-        if constexpr (E >= 4) if (jj == 2) inlane_stage<E, 2>(s, id, k, P, lane);
-        if constexpr (E >= 8) if (jj == 4) inlane_stage<E, 4>(s, id, k, P, lane);
-        if constexpr (E >= 16) if (jj == 8) inlane_stage<E, 8>(s, id, k, P, lane);
-      } else {
-        const bool lower = (lane & j) == 0;
+__device__ __forceinline__ void wave_keep_best(const uint64_t (&key)[E], const int (&id)[E], int nk, int* kept,
+                                               int lane) {
+  uint64_t T = 0;
+  for (int b = 63; b >= 0; --b) {
+    const uint64_t cand = T | (1ull << b);
+    int c = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          if (e * 64 < P) {
-            const double os = __shfl_xor(s[e], j);
-            const int oi = __shfl_xor(id[e], j);
-            const bool asc = ((e * 64 + lane) & k) == 0;
-            const bool mine_first = ranks_before_nb(s[e], id[e], os, oi);
-            // the lower position of an ascending pair keeps the better element
-            if (mine_first != (lower == asc)) {
-              s[e] = os;
-              id[e] = oi;
-            }
-          }
-        }
-      }
+    for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
+    if (c >= nk) T = cand;
+  }
+  int above = 0, at = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    above += __popcll(__ballot(key[e] > T));
+    at += __popcll(__ballot(key[e] == T));
+  }
+  const int need = nk - above;  // >= 1 slots at T to keep
+  // when more slots tie at T than are needed, keep those with index <= I, the
+  // need-th smallest index among them (indices of valid slots are distinct)
+  int I = INT_MAX;
+  if (at > need) {
+    int lo = 0, hi = INT_MAX;  // smallest I with #{tied, id <= I} >= need
+    while (lo < hi) {
+      const int mid = lo + (hi - lo) / 2;
+      int c = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] == T && id[e] <= mid));
+      if (c >= need) hi = mid; else lo = mid + 1;
     }
+    I = lo;
+  }
+  int base = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool keep = key[e] > T || (key[e] == T && id[e] <= I);
+    const unsigned long long m = __ballot(keep);
+    if (keep) kept[base + __popcll(m & ((1ull << lane) - 1))] = id[e];
+    base += __popcll(m);
   }
 }
 
@@ -213,19 +215,13 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
       continue;
     }
     if (ranked) {
-      double s[E];
+      uint64_t key[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int p = e * 64 + lane;
-        s[e] = (p < M && id[e] != INT_MAX) ? sm.sc[p] : -__builtin_inf();
+        key[e] = (p < M && id[e] != INT_MAX) ? score_key(sm.sc[p]) : 0ull;
       }
-      int P = 64;
-      while (P < M) P <<= 1;
-      wave_sort<E>(s, id, P, lane);
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (e * 64 + lane < nk) sm.kept[e * 64 + lane] = id[e];
+      wave_keep_best<E>(key, id, nk, sm.kept, lane);
     } else {
       // keep every valid slot, compacted in slot order
       int base = 0;
