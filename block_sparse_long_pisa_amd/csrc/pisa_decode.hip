@@ -181,7 +181,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T
     float x[RPT][VEC];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)  // unconditional loads (clamped rows): all in flight
-      Wide<T>::load(kb + ((int64_t)j * g.bs + min(rsub + i * RP, nvalid - 1)) * D + col, x[i]);
+      Wide<T>::widen(Wide<T>::stream(kb + ((int64_t)j * g.bs + min(rsub + i * RP, nvalid - 1)) * D + col), x[i]);
     float part[NV];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T
     float x[RPT][VEC];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)  // unconditional loads (clamped rows): all in flight
-      Wide<T>::load(vb + ((int64_t)j * g.bs + min(rsub + i * RP, nvalid - 1)) * D + col, x[i]);
+      Wide<T>::widen(Wide<T>::stream(vb + ((int64_t)j * g.bs + min(rsub + i * RP, nvalid - 1)) * D + col), x[i]);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = rsub + i * RP;

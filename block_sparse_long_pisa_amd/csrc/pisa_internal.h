@@ -44,6 +44,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16 bytes of a read-once stream: marked non-temporal so they do not push
+// reused data out of the caches.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Load 16 bytes and widen to fp32: 8 values for bf16, 4 for fp32.
 template <typename T>
 struct Wide;
@@ -53,6 +62,7 @@ template <>
 struct Wide<uint16_t> {
   static constexpr int kVec = 8;
   __device__ __forceinline__ static uint4 raw(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static uint4 stream(const uint16_t* p) { return load_stream16(p); }
   __device__ __forceinline__ static void widen(const uint4& u, float* out) {
     out[0] = bf16lo(u.x); out[1] = bf16hi(u.x);
     out[2] = bf16lo(u.y); out[3] = bf16hi(u.y);
@@ -65,6 +75,7 @@ template <>
 struct Wide<float> {
   static constexpr int kVec = 4;
   __device__ __forceinline__ static uint4 raw(const float* p) { return *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ static uint4 stream(const float* p) { return load_stream16(p); }
   __device__ __forceinline__ static void widen(const uint4& u, float* out) {
     out[0] = __uint_as_float(u.x); out[1] = __uint_as_float(u.y);
     out[2] = __uint_as_float(u.z); out[3] = __uint_as_float(u.w);

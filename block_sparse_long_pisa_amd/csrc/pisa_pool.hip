@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_leaf_kernel(Geo g, const T*
       uint4 raw[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)  // unconditional loads from clamped rows, all in flight
-        raw[u] = Wide<T>::raw(kb + (int64_t)min(r + u * RPI, r1 - 1) * D + col);
+        raw[u] = Wide<T>::stream(kb + (int64_t)min(r + u * RPI, r1 - 1) * D + col);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         float x[VEC];

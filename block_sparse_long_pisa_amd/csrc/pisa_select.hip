@@ -39,7 +39,7 @@ __device__ __forceinline__ void wave_query_mean(const Geo& g, const T* __restric
       // unconditional loads from a clamped (head, row) keep all of them in flight
       const int tt = min(t + u * RPI, total - 1);
       const int h = kvh * g.G + tt / rows;
-      raw[u] = Wide<T>::raw(q + (((int64_t)b * g.Hq + h) * g.N + r0 + tt % rows) * D + col);
+      raw[u] = Wide<T>::stream(q + (((int64_t)b * g.Hq + h) * g.N + r0 + tt % rows) * D + col);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -60,19 +60,21 @@ __device__ __forceinline__ void wave_query_mean(const Geo& g, const T* __restric
   __builtin_amdgcn_wave_barrier();
 }
 
-// One wave per (batch, kv head, query block); four per workgroup.
+// One wave per (batch, kv head, query block); four query blocks of one slab per workgroup.
 template <typename T, int D, int E>
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(Geo g, const T* __restrict__ q,
+__global__ __launch_bounds__(kSelectThreads) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(Geo g, const T* __restrict__ q,
                                                                 const float* __restrict__ pyr,
-                                                                int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
-                                                                int units) {
+                                                                int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
   __shared__ WaveSmem<E, D> smem[kSelectWaves];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: keep the descent scalar
-  const int u = blockIdx.x * kSelectWaves + wave;
-  if (u >= units) return;
-  const int slab = u / g.nb;
-  const int qb = u % g.nb;
+  // consecutive workgroups take consecutive slabs, so that workgroups placed
+  // round-robin on the XCDs keep one slab's pyramid per XCD's L2
+  const int slabs = g.B * g.Hkv;
+  const int slab = blockIdx.x % slabs;
+  const int qb = (blockIdx.x / slabs) * kSelectWaves + wave;
+  if (qb >= g.nb) return;
+  const int u = slab * g.nb + qb;
   if (g.K == 0) {
     if (lane == 0) cnt[u] = 0;
     return;
@@ -83,10 +85,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Geo g, const T* 
 
 template <typename T, int D, int E>
 hipError_t launch_select_e(const Geo& g, const void* q, const float* pyr, int32_t* idx, int32_t* cnt, hipStream_t s) {
-  const int units = g.B * g.Hkv * g.nb;
-  const int blocks = (units + kSelectWaves - 1) / kSelectWaves;
-  hipLaunchKernelGGL((select_kernel<T, D, E>), dim3(blocks), dim3(kSelectThreads), 0, s, g, (const T*)q, pyr, idx, cnt,
-                     units);
+  const int blocks = g.B * g.Hkv * ((g.nb + kSelectWaves - 1) / kSelectWaves);
+  hipLaunchKernelGGL((select_kernel<T, D, E>), dim3(blocks), dim3(kSelectThreads), 0, s, g, (const T*)q, pyr, idx, cnt);
   return hipGetLastError();
 }
 

@@ -105,6 +105,27 @@ __device__ __forceinline__ void wave_keep_best(const uint64_t (&key)[E], const i
   }
 }
 
+// fp64 value of the lane a DPP row control names (both halves moved as dwords).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+
+// Sum over each row of 16 lanes, left in every lane of the row. After the two
+// quad swaps every lane of a quad holds the quad's sum; the half-row mirror then
+// pairs each quad with the other quad of its half-row, and the row mirror each
+// half-row with the other -- the same pairing as exchanges across lane bits
+// 0, 1, 2 and 3, done on the vector ALU instead of through LDS.
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  v += dpp_f64<0x140>(v);  // row_mirror
+  return v;
+}
+
 // Node id held by pool slot p at level l (kept children first, then the
 // complete children of the query block's own ancestor).
 __device__ __forceinline__ int slot_node(int p, int nchild, int f, const int* kept, int anc_first) {
@@ -144,10 +165,7 @@ __device__ __forceinline__ void score_slots(const float* __restrict__ lvl, int M
         acc += qv[e4 * 4 + 2] * (double)x[u][e4].z;
         acc += qv[e4 * 4 + 3] * (double)x[u][e4].w;
       }
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      acc += __shfl_xor(acc, 4);
-      acc += __shfl_xor(acc, 8);
+      acc = row16_sum(acc);
       const int p = base + u * 4 * NWS + grp;
       if (sub == 0 && p < M) sm.sc[p] = use[u] ? acc : -__builtin_inf();
     }
@@ -321,10 +339,7 @@ __device__ void block_descend(const Geo& g, const float* __restrict__ ps, int qb
           acc += qv[e4 * 4 + 2] * (double)x[u][e4].z;
           acc += qv[e4 * 4 + 3] * (double)x[u][e4].w;
         }
-        acc += __shfl_xor(acc, 1);
-        acc += __shfl_xor(acc, 2);
-        acc += __shfl_xor(acc, 4);
-        acc += __shfl_xor(acc, 8);
+        acc = row16_sum(acc);
         const int p = base + u * NG + grp;
         if (sub == 0 && p < M) {
           sm.sc[p] = use[u] ? acc : -__builtin_inf();
