@@ -118,19 +118,52 @@ def decode_scored_nodes(p, cache_len):
 
 
 def decode_bytes(p, cache_len, cnt):
-    """K/V rows attended + pyramid rows scored + q + out, for one step."""
+    """K/V rows attended + pyramid rows scored + q + out, for one step.
+
+    cache_len: one length for every sequence, or a list of per-sequence lengths.
+    """
     bs, s, d = p.block_size, p.sink_len, p.head_dim
-    pos = cache_len - 1
-    qb = pos // bs
+    lens = [int(cache_len)] * cnt.shape[0] if isinstance(cache_len, (int, np_int_types())) else list(cache_len)
     total_keys = 0
+    summaries = 0
     for b in range(cnt.shape[0]):
+        pos = lens[b] - 1
+        qb = pos // bs
         for g in range(cnt.shape[1]):
             c = int(cnt[b, g])
             total_keys += c * bs + min(s, qb * bs) + (pos - qb * bs + 1)  # sink overlap with block 0 ignored
+        summaries += p.heads_kv * decode_scored_nodes(p, lens[b]) * d * 4
     kv = total_keys * d * 2 * 2
-    summaries = p.batch * p.heads_kv * decode_scored_nodes(p, cache_len) * d * 4
     qo = 2 * p.batch * p.heads_q * d * 2
     return kv + summaries + qo
+
+
+def np_int_types():
+    import numpy as np
+
+    return np.integer
+
+
+def append_bytes(p, old_lens, new_lens):
+    """Key rows read and pyramid nodes read and written by one pyramid append."""
+    bs, f, d, L = p.block_size, p.fanout, p.head_dim, p.levels
+    elt = 2 if p.dtype == "bf16" else 4
+    total = 0
+    for a, z in zip(old_lens, new_lens):
+        if not 0 <= a < z <= p.seq_len:
+            continue
+        j0, j1 = a // bs, (z - 1) // bs
+        rows = z - j0 * bs  # rows of the affected leaves
+        nodes_read, nodes_written = 0, j1 - j0 + 1
+        present = j1 + 1
+        lo, hi = j0, j1
+        for _ in range(1, L):
+            na, nz = lo // f, hi // f
+            nodes_read += sum(min(f, present - n * f) for n in range(na, nz + 1))
+            nodes_written += nz - na + 1
+            lo, hi, present = na, nz, -(-present // f)
+        total += p.heads_kv * (rows * d * elt + (nodes_read + nodes_written) * d * 4)
+    return total
 
 
 # ---------------------------------------------------------------------------
@@ -362,6 +395,57 @@ def run_decode(args, dev):
         "GB/s": db / t_dec_ev / 1e9,
         "frac": db / t_dec_ev / HBM_PEAK,
         "traffic": measured_traffic("decode"),
+    }
+
+    # serving step: every sequence at its own length; each step appends one token
+    # per sequence (its key and value are already in the cache), updates the
+    # pyramid and decodes the batch at the new lengths
+    import numpy as np
+
+    nsteps = args.decode_steps + args.warmup
+    rng = np.random.default_rng(dcfg["seed"])
+    base = rng.integers(dp.seq_len // 2, dp.seq_len - nsteps, size=dp.batch)
+    lens_h = np.stack([base + s for s in range(nsteps + 1)]).astype(np.int32)
+    lens_d = torch.from_numpy(lens_h).to(dev)
+
+    def serve(s, ev=None):
+        if ev is not None:
+            ev[0].record()
+        pisa.pyramid_append(dcp, kc, dpyr, lens_d[s], lens_d[s + 1])
+        if ev is not None:
+            ev[1].record()
+        pisa.decode_step_ragged(dcp, dq, kc, vc, dpyr, lens_d[s + 1], out=dout, idx_out=didx, cnt_out=dcnt,
+                                workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for s in range(args.warmup):
+        serve(s)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
+    t0 = time.perf_counter()
+    for i in range(args.decode_steps):
+        serve(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t_srv = (time.perf_counter() - t0) / args.decode_steps
+    t_app = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
+    t_rdec = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    last = args.warmup + args.decode_steps - 1
+    rb = decode_bytes(dp, lens_h[last + 1].tolist(), dcnt.cpu().numpy())
+    ab = append_bytes(dp, lens_h[last].tolist(), lens_h[last + 1].tolist())
+    log(f"serving step {t_srv * 1e6:.1f} us (append {t_app * 1e6:.1f} us, ragged decode {t_rdec * 1e6:.1f} us, "
+        f"{rb / t_rdec / 1e9:.0f} GB/s)")
+    decode["serving"] = {
+        "workload": "64 sequences at lengths uniform in [65536, 131072), one token appended per sequence per step: "
+                    "pyramid append then ragged decode",
+        "us_per_step": t_srv * 1e6,
+        "append_us": t_app * 1e6,
+        "decode_us": t_rdec * 1e6,
+        "tokens_per_s": dp.batch / t_srv,
+        "decode_bytes": rb,
+        "append_bytes": ab,
+        "decode_GB/s": rb / t_rdec / 1e9,
+        "decode_frac": rb / t_rdec / HBM_PEAK,
     }
     return decode
 

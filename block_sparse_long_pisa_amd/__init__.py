@@ -28,6 +28,8 @@ __all__ = [
     "sparse_attn_fwd",
     "decode_workspace_size",
     "decode_step",
+    "decode_step_ragged",
+    "pyramid_append",
     "prefill",
 ]
 
@@ -41,6 +43,8 @@ EXPORTED_SYMBOLS = [
     "pisa_sparse_attn_fwd",
     "pisa_decode_workspace_size",
     "pisa_decode_step",
+    "pisa_decode_step_ragged",
+    "pisa_pyramid_append",
     "pisa_status_string",
     "pisa_last_error",
     "pisa_version",
@@ -117,6 +121,8 @@ def load_library():
         "pisa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, vp, vp, vp],
         "pisa_decode_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
         "pisa_decode_step": [P, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "pisa_decode_step_ragged": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "pisa_pyramid_append": [P, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -278,3 +284,49 @@ def decode_step(p: Problem, q, k_cache, v_cache, pyramid, cache_len: int, out=No
                                 _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(cnt_out), _ptr(workspace),
                                 workspace.numel(), _stream(q)), "pisa_decode_step")
     return out, lse, idx_out, cnt_out
+
+
+def decode_step_ragged(p: Problem, q, k_cache, v_cache, pyramid, cache_lens, out=None, lse=None, want_lse=False,
+                       idx_out=None, cnt_out=None, want_idx=False, workspace=None):
+    """One decode step with a cache length per sequence: cache_lens int32 [B] on the device.
+
+    Returns (out, lse, idx, cnt) as decode_step does.
+    """
+    torch = _torch()
+    lib = load_library()
+    dt = _tdtype(p)
+    nodes = pyramid_layout(p)[-1]
+    _expect(q, (p.batch, p.heads_q, p.head_dim), dt, "q")
+    _expect(k_cache, (p.batch, p.heads_kv, p.seq_len, p.head_dim), dt, "k_cache")
+    _expect(v_cache, (p.batch, p.heads_kv, p.seq_len, p.head_dim), dt, "v_cache")
+    _expect(pyramid, (p.batch, p.heads_kv, nodes, p.head_dim), torch.float32, "pyramid")
+    _expect(cache_lens, (p.batch,), torch.int32, "cache_lens")
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, tuple(q.shape), dt, "out")
+    if lse is None and want_lse:
+        lse = torch.empty((p.batch, p.heads_q), dtype=torch.float32, device=q.device)
+    if idx_out is None and want_idx and p.top_k:
+        idx_out = torch.empty((p.batch, p.heads_kv, p.top_k), dtype=torch.int32, device=q.device)
+    if cnt_out is None and want_idx:
+        cnt_out = torch.empty((p.batch, p.heads_kv), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, decode_workspace_size(p)), dtype=torch.uint8, device=q.device)
+    _check(lib.pisa_decode_step_ragged(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pyramid),
+                                       _ptr(cache_lens), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(cnt_out),
+                                       _ptr(workspace), workspace.numel(), _stream(q)), "pisa_decode_step_ragged")
+    return out, lse, idx_out, cnt_out
+
+
+def pyramid_append(p: Problem, k_cache, pyramid, old_lens, new_lens):
+    """Update `pyramid` in place after tokens [old_lens[b], new_lens[b]) were written to k_cache."""
+    torch = _torch()
+    lib = load_library()
+    nodes = pyramid_layout(p)[-1]
+    _expect(k_cache, (p.batch, p.heads_kv, p.seq_len, p.head_dim), _tdtype(p), "k_cache")
+    _expect(pyramid, (p.batch, p.heads_kv, nodes, p.head_dim), torch.float32, "pyramid")
+    _expect(old_lens, (p.batch,), torch.int32, "old_lens")
+    _expect(new_lens, (p.batch,), torch.int32, "new_lens")
+    _check(lib.pisa_pyramid_append(ctypes.byref(p), _ptr(k_cache), _ptr(pyramid), _ptr(old_lens), _ptr(new_lens),
+                                   _stream(k_cache)), "pisa_pyramid_append")
+    return pyramid

@@ -98,6 +98,24 @@ pisa_status hip_fail(hipError_t e, const char* what) {
   return fail(PISA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Checks shared by both decode entry points (cache_len checked by the caller).
+pisa_status check_decode(const pisa::Geo& g, const void* q, const void* k_cache, const void* v_cache,
+                         const float* pyramid, const void* out, const void* workspace, size_t workspace_bytes) {
+  if (g.G != 1 && g.G != 2 && g.G != 4 && g.G != 8)
+    return fail(PISA_ERR_UNSUPPORTED, "decode supports 1, 2, 4 or 8 query heads per kv head (got %d)", g.G);
+  if (g.N < 1) return fail(PISA_ERR_SHAPE, "seq_len (the cache capacity) must be >= 1");
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || pyramid == nullptr || out == nullptr)
+    return fail(PISA_ERR_NULL, "q, k_cache, v_cache, pyramid or out is NULL");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(pyramid) || !aligned16(out))
+    return fail(PISA_ERR_ALIGN, "q, caches, pyramid and out must be 16-byte aligned");
+  const size_t need = pisa::decode_workspace_bytes(g);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PISA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(PISA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return PISA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -182,22 +200,45 @@ pisa_status pisa_decode_step(const pisa_problem* p, const void* q, const void* k
   pisa_status s = make_geo(p, &g);
   if (s != PISA_OK) return s;
   if (g.B == 0) return ok();
-  if (g.G != 1 && g.G != 2 && g.G != 4 && g.G != 8)
-    return fail(PISA_ERR_UNSUPPORTED, "decode supports 1, 2, 4 or 8 query heads per kv head (got %d)", g.G);
   if (cache_len < 1 || cache_len > g.N)
     return fail(PISA_ERR_SHAPE, "cache_len %lld outside [1, seq_len = %d]", (long long)cache_len, g.N);
-  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || pyramid == nullptr || out == nullptr)
-    return fail(PISA_ERR_NULL, "q, k_cache, v_cache, pyramid or out is NULL");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(pyramid) || !aligned16(out))
-    return fail(PISA_ERR_ALIGN, "q, caches, pyramid and out must be 16-byte aligned");
-  const size_t need = pisa::decode_workspace_bytes(g);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(PISA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
-                workspace == nullptr ? (size_t)0 : workspace_bytes);
-  if (((uintptr_t)workspace & 255u) != 0) return fail(PISA_ERR_ALIGN, "workspace must be 256-byte aligned");
-  hipError_t e = pisa::launch_decode(g, q, k_cache, v_cache, pyramid, (int)cache_len, out, lse, idx_out, cnt_out,
-                                     workspace, stream);
+  s = check_decode(g, q, k_cache, v_cache, pyramid, out, workspace, workspace_bytes);
+  if (s != PISA_OK) return s;
+  hipError_t e = pisa::launch_decode(g, q, k_cache, v_cache, pyramid, nullptr, (int)cache_len, out, lse, idx_out,
+                                     cnt_out, workspace, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "pisa_decode_step launch");
+}
+
+pisa_status pisa_decode_step_ragged(const pisa_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                                    const float* pyramid, const int32_t* cache_lens, void* out, float* lse,
+                                    int32_t* idx_out, int32_t* cnt_out, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+  pisa::Geo g;
+  pisa_status s = make_geo(p, &g);
+  if (s != PISA_OK) return s;
+  if (g.B == 0) return ok();
+  if (cache_lens == nullptr) return fail(PISA_ERR_NULL, "cache_lens is NULL");
+  if (((uintptr_t)cache_lens & 3u) != 0) return fail(PISA_ERR_ALIGN, "cache_lens must be 4-byte aligned");
+  s = check_decode(g, q, k_cache, v_cache, pyramid, out, workspace, workspace_bytes);
+  if (s != PISA_OK) return s;
+  hipError_t e = pisa::launch_decode(g, q, k_cache, v_cache, pyramid, cache_lens, 0, out, lse, idx_out, cnt_out,
+                                     workspace, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "pisa_decode_step_ragged launch");
+}
+
+pisa_status pisa_pyramid_append(const pisa_problem* p, const void* k_cache, float* pyramid, const int32_t* old_lens,
+                                const int32_t* new_lens, hipStream_t stream) {
+  pisa::Geo g;
+  pisa_status s = make_geo(p, &g);
+  if (s != PISA_OK) return s;
+  if (empty(g)) return ok();
+  if (k_cache == nullptr || pyramid == nullptr || old_lens == nullptr || new_lens == nullptr)
+    return fail(PISA_ERR_NULL, "k_cache, pyramid, old_lens or new_lens is NULL");
+  if (!aligned16(k_cache) || !aligned16(pyramid)) return fail(PISA_ERR_ALIGN, "k_cache and pyramid must be 16-byte aligned");
+  if ((((uintptr_t)old_lens | (uintptr_t)new_lens) & 3u) != 0)
+    return fail(PISA_ERR_ALIGN, "old_lens and new_lens must be 4-byte aligned");
+  hipError_t e = pisa::launch_pyramid_append(g, k_cache, pyramid, old_lens, new_lens, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "pisa_pyramid_append launch");
 }
 
 }  // extern "C"

@@ -5,6 +5,8 @@
 // online softmax, as the Pulsar Attention page merges per-host partial
 // attentions ("Phase 2 : Encodage de la requête globale").
 //
+// Every sequence has its own cache length (one length for all, or a device
+// array of them), so its own query block, local block and attended walk.
 // Three launches on the caller's stream:
 //   decode_select  one workgroup per (batch, kv head): fp64 mean of the group's
 //                  query rows, descent, block list into the workspace;
@@ -38,9 +40,18 @@ struct DecodeWs {
 // (the decode pyramid comes from HBM) and ranked by counting.
 constexpr int kDecSelThreads = 512;
 
+// Cache length of sequence b: from the per-sequence array when there is one.
+// A length outside [1, capacity] marks a sequence that attends nothing.
+__device__ __forceinline__ int seq_len_of(const Geo& g, const int32_t* lens, int len_all, int b, bool& valid) {
+  const int len = lens != nullptr ? lens[b] : len_all;
+  valid = len >= 1 && len <= g.N;
+  return valid ? len : 1;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kDecSelThreads) void decode_select_kernel(Geo g, const T* __restrict__ q,
-                                                                       const float* __restrict__ pyr, int qb,
+                                                                       const float* __restrict__ pyr,
+                                                                       const int32_t* __restrict__ lens, int len_all,
                                                                        int32_t* __restrict__ idx,
                                                                        int32_t* __restrict__ cnt) {
   __shared__ BlockSmem smem;
@@ -48,6 +59,13 @@ __global__ __launch_bounds__(kDecSelThreads) void decode_select_kernel(Geo g, co
   const int slab = blockIdx.x;
   const int b = slab / g.Hkv;
   const int kvh = slab % g.Hkv;
+  bool valid;
+  const int qb = (seq_len_of(g, lens, len_all, b, valid) - 1) / g.bs;
+  if (!valid) {  // uniform across the workgroup
+    for (int t = threadIdx.x; t < g.K; t += kDecSelThreads) idx[(int64_t)slab * g.K + t] = -1;
+    if (threadIdx.x == 0) cnt[slab] = 0;
+    return;
+  }
   for (int c = threadIdx.x; c < D; c += kDecSelThreads) {
     double s = 0.0;
     for (int hh = 0; hh < g.G; ++hh) {
@@ -128,7 +146,8 @@ __device__ __forceinline__ int butterfly_first(int lane) {
 template <typename T, int D, int G>
 __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T* __restrict__ q,
                                                                   const T* __restrict__ kc, const T* __restrict__ vc,
-                                                                  int qb, int pos, int splits, DecodeWs ws) {
+                                                                  const int32_t* __restrict__ lens, int len_all,
+                                                                  int splits, DecodeWs ws) {
   constexpr int VEC = Wide<T>::kVec;
   constexpr int LPR = D / VEC;                // lanes per cache row
   constexpr int RP = kDecThreads / LPR;       // rows per pass of the workgroup
@@ -147,6 +166,18 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T
   const int b = slab / g.Hkv;
   const int kvh = slab % g.Hkv;
   const int tid = threadIdx.x;
+  bool valid;
+  const int pos = seq_len_of(g, lens, len_all, b, valid) - 1;
+  const int qb = pos / g.bs;
+  if (!valid) {  // an empty partial result (uniform across the workgroup)
+    const int64_t pb0 = ((int64_t)slab * splits + split) * G;
+    for (int e = tid; e < G * D; e += kDecThreads) ws.o[pb0 * D + e] = 0.f;
+    if (tid < G) {
+      ws.m[pb0 + tid] = -__builtin_inff();
+      ws.l[pb0 + tid] = 0.f;
+    }
+    return;
+  }
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int col = (tid % LPR) * VEC;
@@ -318,7 +349,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(Geo g, int splits, Deco
     l += w * ws.l[p];
     o += w * ws.o[p * D + threadIdx.x];
   }
-  const float val = o / l;
+  const float val = l > 0.f ? o / l : 0.f;  // a sequence that attends nothing outputs zeros
   if constexpr (sizeof(T) == 2) ((uint16_t*)out)[(int64_t)bh * D + threadIdx.x] = (uint16_t)f32_to_bf16(val);
   else ((float*)out)[(int64_t)bh * D + threadIdx.x] = val;
   if (lse != nullptr && threadIdx.x == 0) lse[bh] = (mstar + log2f(l)) * kLn2;
@@ -360,23 +391,24 @@ size_t decode_workspace_bytes(const Geo& g) {
 
 template <typename T, int D>
 static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr,
-                                  int cache_len, void* out, float* lse, int32_t* idx_out, int32_t* cnt_out, void* wsb,
-                                  hipStream_t s) {
-  const int splits = decode_splits(g, cache_len);
+                                  const int32_t* lens, int len_all, void* out, float* lse, int32_t* idx_out,
+                                  int32_t* cnt_out, void* wsb, hipStream_t s) {
+  const int splits = decode_splits(g, len_all);
   DecodeWs ws = carve(g, wsb, splits);
   const int slabs = g.B * g.Hkv;
-  const int pos = cache_len - 1;
-  const int qb = pos / g.bs;
-  hipLaunchKernelGGL((decode_select_kernel<T, D>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, (const T*)q, pyr, qb,
-                     ws.idx, ws.cnt);
+  hipLaunchKernelGGL((decode_select_kernel<T, D>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, (const T*)q, pyr, lens,
+                     len_all, ws.idx, ws.cnt);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(splits, slabs);
+  const T* qt = (const T*)q;
+  const T* kt = (const T*)kc;
+  const T* vt = (const T*)vc;
   switch (g.G) {
-    case 1: hipLaunchKernelGGL((decode_attn_kernel<T, D, 1>), grid, dim3(kDecThreads), 0, s, g, (const T*)q, (const T*)kc, (const T*)vc, qb, pos, splits, ws); break;
-    case 2: hipLaunchKernelGGL((decode_attn_kernel<T, D, 2>), grid, dim3(kDecThreads), 0, s, g, (const T*)q, (const T*)kc, (const T*)vc, qb, pos, splits, ws); break;
-    case 4: hipLaunchKernelGGL((decode_attn_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, s, g, (const T*)q, (const T*)kc, (const T*)vc, qb, pos, splits, ws); break;
-    default: hipLaunchKernelGGL((decode_attn_kernel<T, D, 8>), grid, dim3(kDecThreads), 0, s, g, (const T*)q, (const T*)kc, (const T*)vc, qb, pos, splits, ws); break;
+    case 1: hipLaunchKernelGGL((decode_attn_kernel<T, D, 1>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
+    case 2: hipLaunchKernelGGL((decode_attn_kernel<T, D, 2>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
+    case 4: hipLaunchKernelGGL((decode_attn_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
+    default: hipLaunchKernelGGL((decode_attn_kernel<T, D, 8>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -391,13 +423,14 @@ static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, c
   return e;
 }
 
-hipError_t launch_decode(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr, int cache_len,
-                         void* out, float* lse, int32_t* idx, int32_t* cnt, void* ws, hipStream_t s) {
+hipError_t launch_decode(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr,
+                         const int32_t* lens, int cache_len, void* out, float* lse, int32_t* idx, int32_t* cnt, void* ws,
+                         hipStream_t s) {
   if (g.dtype == PISA_BF16)
-    return g.D == 128 ? launch_decode_d<uint16_t, 128>(g, q, kc, vc, pyr, cache_len, out, lse, idx, cnt, ws, s)
-                      : launch_decode_d<uint16_t, 64>(g, q, kc, vc, pyr, cache_len, out, lse, idx, cnt, ws, s);
-  return g.D == 128 ? launch_decode_d<float, 128>(g, q, kc, vc, pyr, cache_len, out, lse, idx, cnt, ws, s)
-                    : launch_decode_d<float, 64>(g, q, kc, vc, pyr, cache_len, out, lse, idx, cnt, ws, s);
+    return g.D == 128 ? launch_decode_d<uint16_t, 128>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws, s)
+                      : launch_decode_d<uint16_t, 64>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws, s);
+  return g.D == 128 ? launch_decode_d<float, 128>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws, s)
+                    : launch_decode_d<float, 64>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws, s);
 }
 
 }  // namespace pisa

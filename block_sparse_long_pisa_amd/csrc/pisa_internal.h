@@ -94,7 +94,13 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* k, const void* v
 // decode: selection of one token per (batch, kv head), split attention, merge
 int decode_splits(const Geo& g, int cache_len);
 size_t decode_workspace_bytes(const Geo& g);
-hipError_t launch_decode(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr, int cache_len,
-                         void* out, float* lse, int32_t* idx, int32_t* cnt, void* ws, hipStream_t s);
+// lens: per-sequence cache lengths on the device, or nullptr for cache_len everywhere
+hipError_t launch_decode(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr,
+                         const int32_t* lens, int cache_len, void* out, float* lse, int32_t* idx, int32_t* cnt, void* ws,
+                         hipStream_t s);
+
+// pyramid update after tokens [old_lens[b], new_lens[b]) were written to the key cache
+hipError_t launch_pyramid_append(const Geo& g, const void* k, float* pyr, const int32_t* old_lens,
+                                 const int32_t* new_lens, hipStream_t s);
 
 }  // namespace pisa

@@ -97,6 +97,87 @@ __global__ __launch_bounds__(D) void pool_coarse_kernel(Geo g, float* __restrict
   pb[(int64_t)(g.off[l] + n) * D + threadIdx.x] = (float)(s / (double)(c1 - c0));
 }
 
+// Update after an append: tokens [len0, len1) of sequence b were written to the
+// key cache. Every node whose tokens meet [len0, len1) is recomputed over its
+// tokens before len1 -- leaves from the key rows, coarser nodes from the
+// children present at len1 -- which leaves the pyramid equal, node for node, to
+// one built over the first len1 tokens. Nodes before len0 are untouched. One
+// workgroup per (batch, kv head); a decode step's append touches one leaf and
+// one node per coarser level.
+template <typename T, int D>
+__global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const T* __restrict__ k,
+                                                                   float* __restrict__ pyr,
+                                                                   const int32_t* __restrict__ old_lens,
+                                                                   const int32_t* __restrict__ new_lens) {
+  constexpr int VEC = Wide<T>::kVec;
+  constexpr int LPR = D / VEC;
+  constexpr int RPI = 64 / LPR;
+  const int slab = blockIdx.x;
+  const int b = slab / g.Hkv;
+  const int len0 = old_lens[b];
+  const int len1 = new_lens[b];
+  if (len0 < 0 || len1 > g.N || len0 >= len1) return;  // nothing appended (uniform across the workgroup)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = (lane % LPR) * VEC;
+  const int rsub = lane / LPR;
+  const T* kb = k + (int64_t)slab * g.N * D;
+  float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
+  int a = len0 / g.bs, z = (len1 - 1) / g.bs;  // affected nodes of the level being built
+  for (int j = a + wave; j <= z; j += kPoolThreads / 64) {
+    const int r0 = j * g.bs;
+    const int r1 = min(len1, r0 + g.bs);
+    double acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+    for (int r = r0 + rsub; r < r1; r += RPI * kUnroll) {
+      uint4 raw[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) raw[u] = Wide<T>::raw(kb + (int64_t)min(r + u * RPI, r1 - 1) * D + col);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float x[VEC];
+        Wide<T>::widen(raw[u], x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += r + u * RPI < r1 ? (double)x[e] : 0.0;
+      }
+    }
+#pragma unroll
+    for (int sh = LPR; sh < 64; sh <<= 1)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], sh);
+    if (rsub == 0) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) pb[(int64_t)j * D + col + e] = (float)(acc[e] / (double)(r1 - r0));
+    }
+  }
+  __syncthreads();
+  int present = z + 1;  // nodes of the level below that hold tokens before len1
+  for (int l = 1; l < g.L; ++l) {
+    const int na = a / g.f, nz = z / g.f;
+    for (int e = threadIdx.x; e < (nz - na + 1) * D; e += kPoolThreads) {
+      const int n = na + e / D, c = e % D;
+      const int c0 = n * g.f;
+      const int c1 = min(c0 + g.f, present);
+      double sum = 0.0;
+      for (int ch = c0; ch < c1; ++ch) sum += (double)pb[(int64_t)(g.off[l - 1] + ch) * D + c];
+      pb[(int64_t)(g.off[l] + n) * D + c] = (float)(sum / (double)(c1 - c0));
+    }
+    __syncthreads();
+    a = na;
+    z = nz;
+    present = (present + g.f - 1) / g.f;
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_append_t(const Geo& g, const void* k, float* pyr, const int32_t* old_lens, const int32_t* new_lens,
+                           hipStream_t s) {
+  hipLaunchKernelGGL((pool_append_kernel<T, D>), dim3(g.B * g.Hkv), dim3(kPoolThreads), 0, s, g, (const T*)k, pyr,
+                     old_lens, new_lens);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_pool_t(const Geo& g, const void* k, float* pyr, hipStream_t s) {
   const int slabs = g.B * g.Hkv;
@@ -114,6 +195,15 @@ hipError_t launch_pool_t(const Geo& g, const void* k, float* pyr, hipStream_t s)
 }
 
 }  // namespace
+
+hipError_t launch_pyramid_append(const Geo& g, const void* k, float* pyr, const int32_t* old_lens,
+                                 const int32_t* new_lens, hipStream_t s) {
+  if (g.dtype == PISA_BF16)
+    return g.D == 128 ? launch_append_t<uint16_t, 128>(g, k, pyr, old_lens, new_lens, s)
+                      : launch_append_t<uint16_t, 64>(g, k, pyr, old_lens, new_lens, s);
+  return g.D == 128 ? launch_append_t<float, 128>(g, k, pyr, old_lens, new_lens, s)
+                    : launch_append_t<float, 64>(g, k, pyr, old_lens, new_lens, s);
+}
 
 hipError_t launch_build_pyramid(const Geo& g, const void* k, float* pyr, hipStream_t s) {
   if (g.dtype == PISA_BF16) {

@@ -153,6 +153,38 @@ pisa_status pisa_decode_step(const pisa_problem* p, const void* q, const void* k
                              const float* pyramid, int64_t cache_len, void* out, float* lse, int32_t* idx_out,
                              int32_t* cnt_out, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* One decode step for a batch whose sequences have different cache lengths
+ * (each sequence's new token sits at its own cache_lens[b] - 1). Same selection,
+ * attended set and split-K merge as pisa_decode_step, per sequence.
+ *   cache_lens: device int32 [batch], read by the kernels (so it may be produced
+ *               on the device, e.g. by the step that appended the tokens);
+ *   all other arguments, the workspace size included, as for pisa_decode_step.
+ * The host cannot check device lengths: a sequence whose length lies outside
+ * [1, seq_len] attends nothing -- its output is zeros, its lse -inf and its
+ * selected-block count 0 -- and the call still succeeds. */
+pisa_status pisa_decode_step_ragged(const pisa_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                                    const float* pyramid, const int32_t* cache_lens, void* out, float* lse,
+                                    int32_t* idx_out, int32_t* cnt_out, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/* Bring the pyramid up to date after tokens were appended to the key cache
+ * ("Le pooling comme première réduction": a node summarises its keys, so only
+ * the nodes holding new keys change).
+ *   k_cache: [batch, heads_kv, seq_len, head_dim], tokens [old_lens[b], new_lens[b])
+ *            of sequence b already written;
+ *   pyramid: fp32 [batch, heads_kv, nodes, head_dim] in the pisa_pyramid_layout
+ *            of seq_len (the capacity), up to date for the first old_lens[b] tokens;
+ *   old_lens, new_lens: device int32 [batch].
+ * Every node whose tokens meet [old_lens[b], new_lens[b]) is recomputed over its
+ * tokens before new_lens[b]: afterwards each node holding tokens before
+ * new_lens[b] equals, bit for bit, what pisa_build_pyramid gives for a cache of
+ * exactly new_lens[b] tokens. Other nodes are not written. A sequence with
+ * old_lens[b] < 0, new_lens[b] > seq_len or old_lens[b] >= new_lens[b] is left
+ * as it is. One workgroup per (batch, kv head): meant for the few tokens a
+ * decode step appends; a long prompt is faster through pisa_build_pyramid. */
+pisa_status pisa_pyramid_append(const pisa_problem* p, const void* k_cache, float* pyramid, const int32_t* old_lens,
+                                const int32_t* new_lens, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* pisa_status_string(pisa_status s);
 

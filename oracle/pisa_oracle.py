@@ -22,7 +22,8 @@ page ("Attention clairsemée PISA : noyaux Triton sans matrice de scores"):
    a 64-token prefix by default) and the query's own block under a causal
    mask.
 4. Decode is the same descent and attention for one new query token whose key
-   and value are already in the cache. The online-softmax merge of partial
+   and value are already in the cache (each sequence of a batch at its own
+   cache length in `decode_ragged`). The online-softmax merge of partial
    results (Pulsar page, "Phase 2 : Encodage de la requête globale") is
    written out in `merge_partials`.
 
@@ -62,6 +63,7 @@ __all__ = [
     "attend",
     "attend_block",
     "decode",
+    "decode_ragged",
     "merge_partials",
     "dense_causal_attention",
 ]
@@ -264,6 +266,33 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pyramid: Seq
                 w, l = _softmax_rows(sm_scale * (q[b, h].astype(np.float64) @ kk.T)[None, :])
                 o[b, h] = (w @ vv)[0]
                 lse[b, h] = l[0]
+    return o, lse, idx, cnt
+
+
+def decode_ragged(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pyramid: Sequence[np.ndarray],
+                  cache_lens: Sequence[int], top_k: int, sink_len: int, block_size: int, fanout: int,
+                  sm_scale: float, batches: Optional[Sequence[int]] = None):
+    """One decode step where sequence b's cache holds cache_lens[b] tokens, its new token last.
+
+    Each sequence is the single-sequence decode at its own length. A length
+    outside [1, capacity] attends nothing: output 0, lse -inf, no blocks (the
+    empty-sum reading of the softmax). Returns o, lse, idx, cnt like `decode`.
+    """
+    B, Hq, d = q.shape
+    cap = k_cache.shape[2]
+    o = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    idx = np.full((B, k_cache.shape[1], top_k), -1, np.int32)
+    cnt = np.zeros((B, k_cache.shape[1]), np.int32)
+    for b in (batches if batches is not None else range(B)):
+        n = int(cache_lens[b])
+        if not 1 <= n <= cap:
+            o[b] = 0.0
+            lse[b] = -np.inf
+            continue
+        ob, lb, ib, cb = decode(q[b:b + 1], k_cache[b:b + 1], v_cache[b:b + 1], [lv[b:b + 1] for lv in pyramid], n,
+                                top_k, sink_len, block_size, fanout, sm_scale)
+        o[b], lse[b], idx[b], cnt[b] = ob[0], lb[0], ib[0], cb[0]
     return o, lse, idx, cnt
 
 

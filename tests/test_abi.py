@@ -130,6 +130,35 @@ def test_decode_validation(lib):
     assert call(100, prob=_p(seq_len=4096, heads_q=32, heads_kv=2)) == EUNSUP  # G = 16
 
 
+def test_ragged_decode_and_append_validation(lib):
+    p = _p(seq_len=4096)
+    n = ctypes.c_size_t(0)
+    assert lib.pisa_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == OK
+    fake = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+
+    def ragged(lens=fake, ws_ptr=ws, ws_bytes=n.value, prob=p, q=fake):
+        return lib.pisa_decode_step_ragged(ctypes.byref(prob), q, fake, fake, fake, lens, fake, None, None, None,
+                                           ws_ptr, ws_bytes, None)
+
+    assert ragged(lens=None) == ENULL
+    assert ragged(lens=ctypes.c_void_p(4098)) == EALIGN
+    assert ragged(q=None) == ENULL
+    assert ragged(ws_bytes=n.value - 1) == EWS
+    assert ragged(prob=_p(seq_len=4096, heads_q=6, heads_kv=2)) == EUNSUP
+    assert ragged(prob=_p(batch=0)) == OK  # empty batch: nothing to do
+
+    def append(k=fake, pyr=fake, old=fake, new=fake, prob=p):
+        return lib.pisa_pyramid_append(ctypes.byref(prob), k, pyr, old, new, None)
+
+    assert append(old=None) == ENULL
+    assert append(pyr=None) == ENULL
+    assert append(new=ctypes.c_void_p(4097)) == EALIGN
+    assert append(k=ctypes.c_void_p(4100)) == EALIGN
+    assert append(prob=_p(seq_len=0)) == OK
+    assert lib.pisa_pyramid_append(None, fake, fake, fake, fake, None) == ENULL
+
+
 def test_status_strings(lib):
     for s in range(7):
         assert lib.pisa_status_string(s)

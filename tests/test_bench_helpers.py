@@ -28,3 +28,16 @@ def test_decode_scored_nodes_match_the_descent_pools():
     tr = []
     oracle.descend(levels, rng.standard_normal(8), p.n_blocks - 1, 32, 64, 128, 8, tr)
     assert sum(len(t["pool"]) for t in tr) == bench.decode_scored_nodes(p, p.seq_len) == 1 + 15 + 127 + 263
+
+
+def test_append_bytes_single_token_by_hand():
+    # one token at position 1000 (block 7 of 128-token blocks, fanout 8, 4 levels):
+    # the leaf re-reads rows 896..1000; level 1 node 0 reads its 8 present children,
+    # level 2 node 0 reads its 1 present child, level 3 node 0 its 1
+    p = gen.config(4)["problem"]
+    rows = 1001 - 7 * 128
+    written = 4  # one node per level
+    read = 8 + 1 + 1
+    want = p.heads_kv * (rows * p.head_dim * 2 + (read + written) * p.head_dim * 4)
+    assert bench.append_bytes(p, [1000], [1001]) == want
+    assert bench.append_bytes(p, [5], [5]) == 0 and bench.append_bytes(p, [-1], [3]) == 0

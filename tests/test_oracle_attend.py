@@ -16,8 +16,8 @@ import torch
 from scipy.special import logsumexp
 
 import gen
-from oracle import (attend, attended_keys, build_pyramid, decode, dense_causal_attention, merge_partials,
-                    query_block_means, select)
+from oracle import (attend, attended_keys, build_pyramid, decode, decode_ragged, dense_causal_attention,
+                    merge_partials, query_block_means, select)
 
 
 def _sdpa(q, k, v, mask, scale):
@@ -171,3 +171,32 @@ def test_decode_selection_matches_prefill_rule_for_single_row_block():
         qbar = query_block_means(qfake, Hkv, bs) * bs  # ...scaled back to the row mean
         sidx, scnt = select(pyr, qbar, K, sink, bs, f)
         assert np.array_equal(idx, sidx[:, :, qb]) and np.array_equal(cnt, scnt[:, :, qb])
+
+
+def test_ragged_decode_all_blocks_is_each_sequence_s_dense_last_row():
+    # every sequence at its own length: with K covering every block, row b is the
+    # last row of dense causal attention over that sequence's first len_b tokens
+    B, Hq, Hkv, cap, d, bs, f, L, sink = 4, 4, 2, 256, 16, 32, 2, 3, 16
+    lens = [256, 1, 97, 33]
+    rng = np.random.default_rng(21)
+    qfull = rng.standard_normal((B, Hq, cap, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    pyr = build_pyramid(k, bs, f, L)
+    qtok = np.stack([qfull[b, :, lens[b] - 1] for b in range(B)])
+    o, lse, idx, cnt = decode_ragged(qtok, k, v, pyr, lens, cap // bs, sink, bs, f, 0.25)
+    for b, n in enumerate(lens):
+        od, lsed = dense_causal_attention(qfull[b:b + 1, :, :n], k[b:b + 1, :, :n], v[b:b + 1, :, :n], 0.25)
+        assert np.max(np.abs(o[b] - od[0, :, -1])) < 1e-12
+        assert np.max(np.abs(lse[b] - lsed[0, :, -1])) < 1e-12
+        assert np.all(cnt[b] == max(0, (n - 1) // bs - sink // bs))  # every earlier block outside the sink
+
+
+def test_ragged_decode_out_of_range_lengths_attend_nothing():
+    B, Hq, Hkv, cap, d = 3, 2, 1, 64, 8
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    pyr = build_pyramid(k, 16, 2, 2)
+    o, lse, idx, cnt = decode_ragged(q, k, k, pyr, [0, 65, -3], 2, 0, 16, 2, 0.5)
+    assert np.all(o == 0.0) and np.all(lse == -np.inf) and np.all(cnt == 0) and np.all(idx == -1)
