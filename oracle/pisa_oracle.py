@@ -62,6 +62,7 @@ __all__ = [
     "attended_keys",
     "attend",
     "attend_block",
+    "attend_backward",
     "decode",
     "decode_ragged",
     "merge_partials",
@@ -230,6 +231,45 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, cnt: np
             o[b, h, r0:r1], lse[b, h, r0:r1] = attend_block(q[b, h, r0:r1], k[b, g], v[b, g], r0, sel,
                                                              sink_len, block_size, sm_scale)
     return o, lse
+
+
+def attend_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, cnt: np.ndarray,
+                    dout: np.ndarray, sink_len: int, block_size: int, sm_scale: float):
+    """Gradients of L = sum(dout * o) for o = attend(q, k, v, idx, cnt), the selection held constant.
+
+    Per query row i with attended keys A(i): s_t = sm_scale q_i.k_t, p = softmax_A(i)(s),
+    o_i = sum_t p_t v_t. Then dv_t += p_t dout_i, dp_t = dout_i.v_t,
+    ds_t = p_t (dp_t - sum_u p_u dp_u), dq_i = sm_scale sum_t ds_t k_t and
+    dk_t += sm_scale ds_t q_i; key and value gradients of a KV head sum over the
+    query heads that share it. Returns dq, dk, dv (fp64, shapes of q, k, v).
+    """
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    nb = -(-N // block_size)
+    dq = np.zeros((B, Hq, N, d))
+    dk = np.zeros((B, Hkv, N, d))
+    dv = np.zeros((B, Hkv, N, d))
+    for b in range(B):
+        for g in range(Hkv):
+            kk, vv = k[b, g].astype(np.float64), v[b, g].astype(np.float64)
+            for qb in range(nb):
+                sel = idx[b, g, qb, :cnt[b, g, qb]].tolist()
+                r0, r1 = qb * block_size, min(N, (qb + 1) * block_size)
+                keys = attended_keys(r1 - 1, sel, sink_len, block_size)
+                pos = np.arange(r0, r1)[:, None]
+                for h in range(g * G, (g + 1) * G):
+                    qq = q[b, h, r0:r1].astype(np.float64)
+                    do = dout[b, h, r0:r1].astype(np.float64)
+                    s = sm_scale * (qq @ kk[keys].T)
+                    s = np.where(keys[None, :] <= pos, s, -np.inf)
+                    p, _ = _softmax_rows(s)
+                    dp = do @ vv[keys].T
+                    ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+                    dq[b, h, r0:r1] = sm_scale * (ds @ kk[keys])
+                    np.add.at(dk[b, g], keys, sm_scale * (ds.T @ qq))
+                    np.add.at(dv[b, g], keys, p.T @ do)
+    return dq, dk, dv
 
 
 # --------------------------------------------------------------------------
