@@ -333,6 +333,38 @@ def run_prefill(args, dev):
         },
     }
 
+    if args.backward:
+        # backward of the same attention: the forward's output and lse, an output
+        # gradient, then dq, dk, dv (selection held constant)
+        lse = torch.empty((p.batch, p.heads_q, p.seq_len), dtype=torch.float32, device=dev)
+        pisa.sparse_attn_fwd(cp, q, k, v, idx, cnt, out, lse)
+        dout = torch.randn_like(q)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = torch.empty(pisa.sparse_attn_bwd_workspace_size(cp), dtype=torch.uint8, device=dev)
+        for _ in range(args.warmup):
+            pisa.sparse_attn_bwd(cp, q, k, v, idx, cnt, out, lse, dout, dq, dk, dv, workspace=bws)
+        torch.cuda.synchronize()
+        be = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.backward_steps)]
+        for e in be:
+            e[0].record()
+            pisa.sparse_attn_bwd(cp, q, k, v, idx, cnt, out, lse, dout, dq, dk, dv, workspace=bws)
+            e[1].record()
+        torch.cuda.synchronize()
+        t_bwd = float(np.mean([e[0].elapsed_time(e[1]) for e in be])) * 1e-3
+        bflops = 10.0 * p.head_dim * pairs  # S, dP, dV, dK, dQ products over the attended pairs
+        log(f"backward {t_bwd * 1e3:.3f} ms ({bflops / t_bwd / 1e12:.1f} TFLOP/s)")
+        result["backward"] = {
+            "workload": "gradients dq, dk, dv of the same 128K GQA sparse attention (selection held constant)",
+            "ms": t_bwd * 1e3,
+            "steps": args.backward_steps,
+            "bound": "mfma",
+            "algorithmic_flops": bflops,
+            "TFLOP/s": bflops / t_bwd / 1e12,
+            "frac": bflops / t_bwd / BF16_PEAK,
+            "workspace_bytes": bws.numel(),
+        }
+        del dout, dq, dk, dv, bws, lse
+
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
         bcopy = torch.empty_like(a)
@@ -460,6 +492,10 @@ def main(argv=None):
     ap.add_argument("--only", choices=["prefill", "decode"], default=None,
                     help="run one workload only (profiling); the JSON line then lacks the other")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", dest="backward", action="store_true", default=True,
+                    help="also time the backward pass on the prefill workload (default)")
+    ap.add_argument("--no-backward", dest="backward", action="store_false")
+    ap.add_argument("--backward-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args(argv)

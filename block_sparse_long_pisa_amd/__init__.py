@@ -26,6 +26,8 @@ __all__ = [
     "build_pyramid",
     "select_topk",
     "sparse_attn_fwd",
+    "sparse_attn_bwd_workspace_size",
+    "sparse_attn_bwd",
     "decode_workspace_size",
     "decode_step",
     "decode_step_ragged",
@@ -41,6 +43,8 @@ EXPORTED_SYMBOLS = [
     "pisa_build_pyramid",
     "pisa_select_topk",
     "pisa_sparse_attn_fwd",
+    "pisa_sparse_attn_bwd_workspace_size",
+    "pisa_sparse_attn_bwd",
     "pisa_decode_workspace_size",
     "pisa_decode_step",
     "pisa_decode_step_ragged",
@@ -120,6 +124,8 @@ def load_library():
         "pisa_select_topk": [P, vp, vp, vp, vp, vp],
         "pisa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, vp, vp, vp],
         "pisa_decode_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
+        "pisa_sparse_attn_bwd_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
+        "pisa_sparse_attn_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "pisa_decode_step": [P, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "pisa_decode_step_ragged": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "pisa_pyramid_append": [P, vp, vp, vp, vp, vp],
@@ -249,6 +255,43 @@ def prefill(p: Problem, q, k, v, want_lse: bool = False):
     idx, cnt = select_topk(p, q, pyr)
     out, lse = sparse_attn_fwd(p, q, k, v, idx, cnt, want_lse=want_lse)
     return out, lse, idx, cnt, pyr
+
+
+def sparse_attn_bwd_workspace_size(p: Problem) -> int:
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _check(lib.pisa_sparse_attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)),
+           "pisa_sparse_attn_bwd_workspace_size")
+    return n.value
+
+
+def sparse_attn_bwd(p: Problem, q, k, v, idx, cnt, out, lse, dout, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of the sparse attention for output gradient dout; the selection is held constant."""
+    torch = _torch()
+    lib = load_library()
+    dt = _tdtype(p)
+    nb = p.n_blocks
+    _expect(q, (p.batch, p.heads_q, p.seq_len, p.head_dim), dt, "q")
+    _expect(k, (p.batch, p.heads_kv, p.seq_len, p.head_dim), dt, "k")
+    _expect(v, (p.batch, p.heads_kv, p.seq_len, p.head_dim), dt, "v")
+    _expect(cnt, (p.batch, p.heads_kv, nb), torch.int32, "cnt")
+    if p.top_k:
+        _expect(idx, (p.batch, p.heads_kv, nb, p.top_k), torch.int32, "idx")
+    _expect(out, tuple(q.shape), dt, "out")
+    _expect(lse, (p.batch, p.heads_q, p.seq_len), torch.float32, "lse")
+    _expect(dout, tuple(q.shape), dt, "dout")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _expect(dq, tuple(q.shape), dt, "dq")
+    _expect(dk, tuple(k.shape), dt, "dk")
+    _expect(dv, tuple(v.shape), dt, "dv")
+    if workspace is None:
+        workspace = torch.empty(max(1, sparse_attn_bwd_workspace_size(p)), dtype=torch.uint8, device=q.device)
+    _check(lib.pisa_sparse_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx) if p.top_k else None,
+                                    _ptr(cnt), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                    _ptr(workspace), workspace.numel(), _stream(q)), "pisa_sparse_attn_bwd")
+    return dq, dk, dv
 
 
 def decode_workspace_size(p: Problem) -> int:

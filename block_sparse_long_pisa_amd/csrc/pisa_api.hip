@@ -184,6 +184,40 @@ pisa_status pisa_sparse_attn_fwd(const pisa_problem* p, const void* q, const voi
   return e == hipSuccess ? ok() : hip_fail(e, "pisa_sparse_attn_fwd launch");
 }
 
+pisa_status pisa_sparse_attn_bwd_workspace_size(const pisa_problem* p, size_t* bytes) {
+  pisa::Geo g;
+  pisa_status s = make_geo(p, &g);
+  if (s != PISA_OK) return s;
+  if (bytes == nullptr) return fail(PISA_ERR_NULL, "bytes is NULL");
+  *bytes = empty(g) ? 0 : pisa::attn_bwd_workspace_bytes(g);
+  return ok();
+}
+
+pisa_status pisa_sparse_attn_bwd(const pisa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
+                                 const int32_t* cnt, const void* out, const float* lse, const void* dout, void* dq,
+                                 void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  pisa::Geo g;
+  pisa_status s = make_geo(p, &g);
+  if (s != PISA_OK) return s;
+  if (empty(g)) return ok();
+  if (g.dtype != PISA_BF16) return fail(PISA_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 only");
+  if (q == nullptr || k == nullptr || v == nullptr || cnt == nullptr || out == nullptr || lse == nullptr ||
+      dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || (idx == nullptr && g.K > 0))
+    return fail(PISA_ERR_NULL, "q, k, v, idx, cnt, out, lse, dout, dq, dk or dv is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || ((uintptr_t)lse & 3u) != 0)
+    return fail(PISA_ERR_ALIGN, "tensors must be 16-byte aligned (lse 4-byte)");
+  if ((int64_t)g.B * g.Hkv * g.nb > INT32_MAX / 2)
+    return fail(PISA_ERR_UNSUPPORTED, "too many key blocks for the backward pass");
+  const size_t need = pisa::attn_bwd_workspace_bytes(g);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PISA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  if (((uintptr_t)workspace & 255u) != 0) return fail(PISA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  hipError_t e = pisa::launch_attn_bwd(g, q, k, v, idx, cnt, out, lse, dout, dq, dk, dv, workspace, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "pisa_sparse_attn_bwd launch");
+}
+
 pisa_status pisa_decode_workspace_size(const pisa_problem* p, size_t* bytes) {
   pisa::Geo g;
   pisa_status s = make_geo(p, &g);

@@ -19,154 +19,10 @@
 // online softmax in registers, and accumulates O^T += V^T P^T on the same
 // matrix cores, reading V^T fragments with gfx950's transposing LDS reads.
 // fp32 path: plain VALU, one thread per query row.
-#include "pisa_internal.h"
+#include "pisa_attn_common.h"
 
 namespace pisa {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-// 2^x with the hardware's v_exp_f32 and no denormal range reduction: results
-// below 2^-126 only ever weigh a softmax term that is negligible anyway.
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Reductions across the two half-waves (lanes l and l ^ 32): v_permlane32_swap
-// exchanges one half of its first operand with the other half of its second, so
-// with x in both operands the two results hold x of both halves in every lane.
-__device__ __forceinline__ float max_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Which key block a tile index refers to, and how many of its keys count.
-struct TileWalk {
-  int nfull_sink;    // blocks wholly inside the sink (before qb)
-  int partial;       // 1 if the block holding the sink's end is attended as a sink tile
-  int nsel;          // selected blocks
-  int ntiles;        // + 1 local block
-  __device__ __forceinline__ void at(int t, const int* sel, const Geo& g, int qb, int local_rows, int& j, int& nvalid,
-                                     bool& local) const {
-    local = false;
-    if (t < nfull_sink) {
-      j = t;
-      nvalid = g.bs;
-    } else if (t < nfull_sink + partial) {
-      j = g.j0;
-      nvalid = g.sink - g.j0 * g.bs;
-    } else if (t < ntiles - 1) {
-      j = sel[t - nfull_sink - partial];
-      nvalid = g.bs;
-      if (j < 0 || j >= qb) {  // not a block this unit may select: attend nothing from it
-        j = qb;
-        nvalid = 0;
-      }
-    } else {
-      j = qb;
-      nvalid = local_rows;
-      local = true;
-    }
-  }
-};
-
-__device__ __forceinline__ TileWalk make_walk(const Geo& g, int qb, const int* sel, int nsel) {
-  TileWalk w;
-  w.nfull_sink = min(g.j0, qb);
-  const bool sink_tail = g.sink > g.j0 * g.bs && g.j0 < qb;
-  w.partial = (sink_tail && !(nsel > 0 && sel[0] == g.j0)) ? 1 : 0;
-  w.nsel = nsel;
-  w.ntiles = w.nfull_sink + w.partial + nsel + 1;
-  return w;
-}
-
-// LDS tiles hold key rows with padded pitches chosen so that both read
-// patterns are free of bank conflicts: K rows are D + 8 bf16 apart (16
-// consecutive rows at one 16-byte chunk land on distinct banks), V rows D + 32
-// apart (4 consecutive rows x 64 bytes, the transposing V^T reads, cover all
-// banks once). Every read is then a per-lane base register plus an immediate.
-template <int D, int BS = 128>
-struct TilePitch {
-  static constexpr int K = D + 8;   // bf16 elements per K row
-  static constexpr int V = D + 32;  // bf16 elements per V row
-  static constexpr int KU = K / 8;  // 16-byte units per K row
-  static constexpr int VU = V / 8;
-  // whole 1 KB wave copies per tile; the LDS arrays are sized to match
-  static constexpr int KI = (BS * KU + 63) / 64;
-  static constexpr int VI = (BS * VU + 63) / 64;
-  static constexpr int KSIZE = KI * 512;  // bf16 elements
-  static constexpr int VSIZE = VI * 512;
-};
-
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
-
-// Source offset (elements) within a tile of the 16-byte unit u of a padded LDS
-// tile; padding units (and the slack past the tile) re-read the row's first
-// chunk, rows past `rows` re-read the last valid row (their keys are masked).
-template <int D, int UPR>
-__device__ __forceinline__ int unit_src(int u, int rows) {
-  const int r = u / UPR, cu = u % UPR;
-  return min(r, rows - 1) * D + (cu < D / 8 ? cu : 0) * 8;
-}
-
-// Per-lane source offsets of this wave's copies of a full tile (they do not
-// change from tile to tile).
-template <int D, int BS, int NW>
-struct DmaPlan {
-  using TP = TilePitch<D, BS>;
-  static constexpr int KN = (TP::KI + NW - 1) / NW;
-  static constexpr int VN = (TP::VI + NW - 1) / NW;
-  int k[KN];
-  int v[VN];
-  __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-    for (int n = 0; n < KN; ++n) k[n] = unit_src<D, TP::KU>((wave + NW * n) * 64 + lane, BS);
-#pragma unroll
-    for (int n = 0; n < VN; ++n) v[n] = unit_src<D, TP::VU>((wave + NW * n) * 64 + lane, BS);
-  }
-};
-
-// Issue the asynchronous global->LDS copies of one K and one V tile (block j).
-// Each wave instruction fills 64 consecutive 16-byte LDS units in row order.
-template <int D, int BS, int NW>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
-                                           int rows_in_mem, uint16_t* kdst, uint16_t* vdst, int wave, int lane,
-                                           const DmaPlan<D, BS, NW>& plan) {
-  using TP = TilePitch<D, BS>;
-  using PL = DmaPlan<D, BS, NW>;
-  // a planned offset row * D + col keeps its column; rows past the last valid
-  // one (only in a sequence's ragged last block) move to the last valid row
-  const int last = (rows_in_mem - 1) * D;
-#pragma unroll
-  for (int n = 0; n < PL::KN; ++n) {
-    const int i = wave + NW * n;
-    if (i < TP::KI) {
-      const int off = min(plan.k[n], last + (plan.k[n] & (D - 1)));
-      __builtin_amdgcn_global_load_lds(kt + off, (lds_void_ptr)(kdst + i * 512), 16, 0, 0);
-    }
-  }
-#pragma unroll
-  for (int n = 0; n < PL::VN; ++n) {
-    const int i = wave + NW * n;
-    if (i < TP::VI) {
-      const int off = min(plan.v[n], last + (plan.v[n] & (D - 1)));
-      __builtin_amdgcn_global_load_lds(vt + off, (lds_void_ptr)(vdst + i * 512), 16, 0, 0);
-    }
-  }
-}
-
-__device__ __forceinline__ void wait_loads_and_sync() {
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0) only (expcnt, lgkmcnt left free)
-  __syncthreads();                            // ... and every other wave's
-}
 
 template <int D, int BS>
 struct AttnState {

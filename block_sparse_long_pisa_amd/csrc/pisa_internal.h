@@ -91,6 +91,12 @@ hipError_t launch_select(const Geo& g, const void* q, const float* pyr, int32_t*
 hipError_t launch_attn(const Geo& g, const void* q, const void* k, const void* v, const int32_t* idx,
                        const int32_t* cnt, void* out, float* lse, hipStream_t s);
 
+// backward of the sparse attention (bf16): rowdot, dQ, key lists, dK/dV, reduce
+size_t attn_bwd_workspace_bytes(const Geo& g);
+hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const void* v, const int32_t* idx,
+                           const int32_t* cnt, const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                           void* dv, void* ws, hipStream_t s);
+
 // decode: selection of one token per (batch, kv head), split attention, merge
 int decode_splits(const Geo& g, int cache_len);
 size_t decode_workspace_bytes(const Geo& g);

@@ -133,6 +133,28 @@ pisa_status pisa_select_topk(const pisa_problem* p, const void* q, const float* 
 pisa_status pisa_sparse_attn_fwd(const pisa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
                                  const int32_t* cnt, void* out, float* lse, hipStream_t stream);
 
+/* Device workspace (bytes) that pisa_sparse_attn_bwd needs for this problem. */
+pisa_status pisa_sparse_attn_bwd_workspace_size(const pisa_problem* p, size_t* bytes);
+
+/* Gradients of the sparse attention with the selection held constant (the PISA
+ * page, "Attention clairsemée PISA : noyaux Triton sans matrice de scores",
+ * presents its kernels for training as well as inference).
+ *   q, k, v, idx, cnt: as given to pisa_sparse_attn_fwd (idx ascending and
+ *            distinct within a row, as pisa_select_topk writes it);
+ *   out, lse: that call's output and its lse (lse is required here);
+ *   dout: gradient of the loss with respect to out, like q;
+ *   dq: like q; dk, dv: like k, v -- all written, none accumulated into;
+ *   workspace: device memory of at least pisa_sparse_attn_bwd_workspace_size
+ *              bytes, 256-byte aligned.
+ * For query i with attended keys A(i), p = exp(sm_scale q_i.k_t - lse_i),
+ * dS = p (dout_i.v_t - dout_i.out_i); dq_i = sm_scale sum_t dS k_t,
+ * dk_t = sm_scale sum_i dS q_i, dv_t = sum_i p dout_i (key and value gradients
+ * sum over the query heads of the group). bf16 only: fp32 problems return
+ * PISA_ERR_UNSUPPORTED. Results are deterministic (no atomics). */
+pisa_status pisa_sparse_attn_bwd(const pisa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
+                                 const int32_t* cnt, const void* out, const float* lse, const void* dout, void* dq,
+                                 void* dk, void* dv, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Device workspace (bytes) that pisa_decode_step needs for this problem. */
 pisa_status pisa_decode_workspace_size(const pisa_problem* p, size_t* bytes);
 

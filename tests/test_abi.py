@@ -159,6 +159,27 @@ def test_ragged_decode_and_append_validation(lib):
     assert lib.pisa_pyramid_append(None, fake, fake, fake, fake, None) == ENULL
 
 
+def test_backward_validation(lib):
+    p = _p(seq_len=4096)
+    n = ctypes.c_size_t(0)
+    assert lib.pisa_sparse_attn_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == OK and n.value > 0
+    assert lib.pisa_sparse_attn_bwd_workspace_size(ctypes.byref(p), None) == ENULL
+    fake = ctypes.c_void_p(4096)
+    ws = ctypes.c_void_p(1 << 20)
+
+    def bwd(prob=p, lse=fake, dq=fake, ws_ptr=ws, ws_bytes=n.value, k=fake):
+        return lib.pisa_sparse_attn_bwd(ctypes.byref(prob), fake, k, fake, fake, fake, fake, lse, fake, dq, fake, fake,
+                                        ws_ptr, ws_bytes, None)
+
+    assert bwd(lse=None) == ENULL
+    assert bwd(dq=None) == ENULL
+    assert bwd(k=ctypes.c_void_p(4104)) == EALIGN
+    assert bwd(ws_bytes=n.value - 1) == EWS
+    assert bwd(ws_ptr=ctypes.c_void_p((1 << 20) + 64)) == EALIGN
+    assert bwd(prob=_p(seq_len=4096, dtype=pisa.F32)) == EUNSUP
+    assert bwd(prob=_p(batch=0)) == OK
+
+
 def test_status_strings(lib):
     for s in range(7):
         assert lib.pisa_status_string(s)
