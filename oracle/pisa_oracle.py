@@ -96,11 +96,26 @@ def _mean_groups(x: np.ndarray, group: int) -> np.ndarray:
     return sums / counts[:, None]
 
 
-def build_pyramid(k: np.ndarray, block_size: int, fanout: int, levels: int) -> List[np.ndarray]:
-    """Key pyramid of a [B, H, N, d] key tensor: a list of fp32 arrays [B, H, nodes_l, d]."""
-    pyr = [_mean_groups(k, block_size).astype(np.float32)]
+def _max_groups(x: np.ndarray, group: int) -> np.ndarray:
+    """Element-wise max of consecutive groups of `group` rows along axis -2 (last group may be short)."""
+    n = x.shape[-2]
+    ng = -(-n // group)
+    out = np.empty(x.shape[:-2] + (ng, x.shape[-1]), dtype=np.float64)
+    for i in range(ng):
+        out[..., i, :] = x[..., i * group:min(n, (i + 1) * group), :].astype(np.float64).max(axis=-2)
+    return out
+
+
+def build_pyramid(k: np.ndarray, block_size: int, fanout: int, levels: int, pool: str = "mean") -> List[np.ndarray]:
+    """Key pyramid of a [B, H, N, d] key tensor: a list of fp32 arrays [B, H, nodes_l, d].
+
+    pool "mean" (the default) summarises a node by the mean of its keys; "max"
+    (a variant) by their element-wise maximum, which folds exactly level by level.
+    """
+    group = _mean_groups if pool == "mean" else _max_groups
+    pyr = [group(k, block_size).astype(np.float32)]
     for _ in range(1, levels):
-        pyr.append(_mean_groups(pyr[-1], fanout).astype(np.float32))
+        pyr.append(group(pyr[-1], fanout).astype(np.float32))
     return pyr
 
 
@@ -122,14 +137,43 @@ def _top(nodes: Sequence[int], scores: np.ndarray, k: int) -> List[int]:
     return [nodes[i] for i in order[:k]]
 
 
+def _descend_bidirectional(levels, qbar, qb, top_k, sink_len, block_size, fanout, trace):
+    """Non-causal variant: the candidates are every block outside the sink except
+    the query block itself; a node is scored if it holds a candidate, so the top
+    level starts with all of them and each level expands the kept nodes only."""
+    L = len(levels)
+    nb = levels[0].shape[0]
+    j0 = sink_len // block_size
+    span = [fanout ** l for l in range(L)]
+
+    def useful(n: int, l: int) -> bool:
+        lo, hi = max(n * span[l], j0), min((n + 1) * span[l], nb)
+        return hi - lo - (1 if lo <= qb < hi else 0) > 0
+
+    pool = [n for n in range(levels[L - 1].shape[0]) if useful(n, L - 1)]
+    for l in range(L - 1, -1, -1):
+        scores = levels[l][pool].astype(np.float64) @ qbar if pool else np.zeros(0)
+        kept = _top(pool, scores, top_k)
+        if trace is not None:
+            trace.append(dict(level=l, pool=list(pool), scores=scores, kept=list(kept)))
+        if l == 0:
+            return sorted(kept)
+        below = levels[l - 1].shape[0]
+        pool = sorted(c for n in kept for c in range(n * fanout, min((n + 1) * fanout, below)) if useful(c, l - 1))
+    raise AssertionError("unreachable")
+
+
 def descend(levels: Sequence[np.ndarray], qbar: np.ndarray, qb: int, top_k: int, sink_len: int,
-            block_size: int, fanout: int, trace: Optional[list] = None) -> List[int]:
+            block_size: int, fanout: int, trace: Optional[list] = None, causal: bool = True) -> List[int]:
     """Selected key blocks (ascending) for query block `qb`.
 
     `levels[l]` is the [nodes_l, d] pyramid level of one (batch, KV head);
     `qbar` the fp64 query representative. If `trace` is a list, one dict per
-    level (pool, scores, kept) is appended to it.
+    level (pool, scores, kept) is appended to it. causal=False: the
+    bidirectional variant (`_descend_bidirectional`).
     """
+    if not causal:
+        return _descend_bidirectional(levels, qbar, qb, top_k, sink_len, block_size, fanout, trace)
     L = len(levels)
     j0 = sink_len // block_size  # blocks wholly inside the sink
     span = [fanout ** l for l in range(L)]  # blocks under one node of level l
@@ -153,7 +197,7 @@ def descend(levels: Sequence[np.ndarray], qbar: np.ndarray, qb: int, top_k: int,
 
 
 def select(pyramid: Sequence[np.ndarray], qbar: np.ndarray, top_k: int, sink_len: int, block_size: int,
-           fanout: int, traces: Optional[dict] = None):
+           fanout: int, traces: Optional[dict] = None, causal: bool = True):
     """Selection for every (batch, KV head, query block).
 
     Returns idx int32 [B, Hkv, nb, K] (ascending, -1 padded) and cnt int32 [B, Hkv, nb].
@@ -166,7 +210,7 @@ def select(pyramid: Sequence[np.ndarray], qbar: np.ndarray, top_k: int, sink_len
             lv = [p[b, g] for p in pyramid]
             for qb in range(nb):
                 tr = [] if traces is not None else None
-                sel = descend(lv, qbar[b, g, qb], qb, top_k, sink_len, block_size, fanout, tr)
+                sel = descend(lv, qbar[b, g, qb], qb, top_k, sink_len, block_size, fanout, tr, causal)
                 cnt[b, g, qb] = len(sel)
                 idx[b, g, qb, :len(sel)] = sel
                 if traces is not None:
@@ -178,14 +222,26 @@ def select(pyramid: Sequence[np.ndarray], qbar: np.ndarray, top_k: int, sink_len
 # 3. exact attention over the attended set
 
 
-def attended_keys(i: int, sel: Sequence[int], sink_len: int, block_size: int) -> np.ndarray:
-    """Sorted key positions attended by the query at absolute position i."""
+def attended_keys(i: int, sel: Sequence[int], sink_len: int, block_size: int, causal: bool = True,
+                  n: Optional[int] = None) -> np.ndarray:
+    """Sorted key positions attended by the query at absolute position i.
+
+    Causal: ([0, sink) U selected blocks U [qb*bs, i]) intersected with [0, i].
+    Non-causal (sequence length n): [0, sink) U selected blocks U the whole block
+    qb, intersected with [0, n).
+    """
     qb = i // block_size
-    keys = set(range(min(sink_len, i + 1)))
+    if causal:
+        keys = set(range(min(sink_len, i + 1)))
+        for j in sel:
+            keys.update(range(j * block_size, (j + 1) * block_size))
+        keys.update(range(qb * block_size, i + 1))
+        return np.array(sorted(t for t in keys if t <= i), dtype=np.int64)
+    keys = set(range(min(sink_len, n)))
     for j in sel:
-        keys.update(range(j * block_size, (j + 1) * block_size))
-    keys.update(range(qb * block_size, i + 1))
-    return np.array(sorted(t for t in keys if t <= i), dtype=np.int64)
+        keys.update(range(j * block_size, min(n, (j + 1) * block_size)))
+    keys.update(range(qb * block_size, min(n, (qb + 1) * block_size)))
+    return np.array(sorted(keys), dtype=np.int64)
 
 
 def _softmax_rows(s: np.ndarray):
@@ -196,23 +252,24 @@ def _softmax_rows(s: np.ndarray):
 
 
 def attend_block(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, row0: int, sel: Sequence[int],
-                 sink_len: int, block_size: int, sm_scale: float):
+                 sink_len: int, block_size: int, sm_scale: float, causal: bool = True):
     """Attention for consecutive query rows q_rows[r] at positions row0 + r (all in one block).
 
     k, v: [N, d] of the query's KV head. Returns (o fp64 [R, d], lse fp64 [R]).
     """
     R = q_rows.shape[0]
     last = row0 + R - 1
-    keys = attended_keys(last, sel, sink_len, block_size)  # superset for every row of the block
+    keys = attended_keys(last, sel, sink_len, block_size, causal, k.shape[0])  # superset for every row
     s = sm_scale * (q_rows.astype(np.float64) @ k[keys].astype(np.float64).T)
-    pos = row0 + np.arange(R)[:, None]
-    s = np.where(keys[None, :] <= pos, s, -np.inf)  # causal: key position <= query position
+    if causal:
+        pos = row0 + np.arange(R)[:, None]
+        s = np.where(keys[None, :] <= pos, s, -np.inf)  # key position <= query position
     w, lse = _softmax_rows(s)
     return w @ v[keys].astype(np.float64), lse
 
 
 def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, cnt: np.ndarray, sink_len: int,
-           block_size: int, sm_scale: float, blocks: Optional[Sequence] = None):
+           block_size: int, sm_scale: float, blocks: Optional[Sequence] = None, causal: bool = True):
     """Sparse attention output o [B, Hq, N, d] fp64 and lse [B, Hq, N].
 
     `blocks`, if given, is a list of (b, g, qb) units to compute; other rows stay NaN.
@@ -229,7 +286,7 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, cnt: np
         r0, r1 = qb * block_size, min(N, (qb + 1) * block_size)
         for h in range(g * G, (g + 1) * G):
             o[b, h, r0:r1], lse[b, h, r0:r1] = attend_block(q[b, h, r0:r1], k[b, g], v[b, g], r0, sel,
-                                                             sink_len, block_size, sm_scale)
+                                                             sink_len, block_size, sm_scale, causal)
     return o, lse
 
 

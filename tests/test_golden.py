@@ -25,7 +25,7 @@ def _levels(case):
 def test_hand_worked_descent(case):
     tr = []
     sel = descend(_levels(case), np.array([float(case["qbar"])]), case["query_block"], case["top_k"],
-                  case["sink_blocks"] * BS, BS, case["fanout"], tr)
+                  case["sink_blocks"] * BS, BS, case["fanout"], tr, case.get("causal", True))
     assert sel == case["selected"]
     assert [t["pool"] for t in tr] == case["pools"]
 
@@ -48,3 +48,10 @@ def test_hand_worked_attended_set_and_output(case):
     q = np.ones((1, 1))
     o, _ = attend_block(q, k, v, i, case["selected"], s, bs, 1.0)
     assert o[0, 0] == pytest.approx(case["output_if_value_is_position"], abs=1e-12)
+
+
+@pytest.mark.parametrize("case", GOLDEN["pyramids"], ids=lambda c: c["name"])
+def test_hand_worked_max_pyramid(case):
+    k = np.asarray(case["rows"], np.float32)[None, None, :, None]
+    lv = build_pyramid(k, case["block_size"], case["fanout"], case["levels"], pool="max")
+    assert [x[0, 0, :, 0].tolist() for x in lv] == case["levels_max"]

@@ -165,7 +165,8 @@ def _golden():
         return json.load(f)
 
 
-@pytest.mark.parametrize("case", _golden()["descents"], ids=lambda c: c["name"])
+@pytest.mark.parametrize("case", [c for c in _golden()["descents"] if c.get("causal", True)],
+                         ids=lambda c: c["name"])
 def test_hand_worked_descents_on_gpu(case):
     """The hand-worked descents, embedded in the first of 64 dimensions with 32-token blocks."""
     bs, d = 32, 64
