@@ -89,6 +89,26 @@ def attended_pairs(p, idx, cnt):
     return total
 
 
+def attended_pairs_bidirectional(p, idx, cnt):
+    """Sum over query rows of |attended keys| for the non-causal variant (exact integers)."""
+    import numpy as np
+
+    bs, N, G = p.block_size, p.seq_len, p.group
+    s = min(p.sink_len, N)
+    j0 = p.sink_len // bs
+    nb = p.n_blocks
+    size = np.minimum(bs, N - np.arange(nb) * bs).astype(np.int64)  # keys per block
+    sink_in = np.clip(np.minimum(s, (np.arange(nb) + 1) * bs) - np.arange(nb) * bs, 0, None)  # keys of block j in the sink
+    total = 0
+    for b in range(cnt.shape[0]):
+        for g in range(cnt.shape[1]):
+            for qb in range(nb):
+                sel = idx[b, g, qb, :cnt[b, g, qb]]
+                keys = s + int(size[sel].sum() - sink_in[sel].sum()) + int(size[qb] - sink_in[qb])
+                total += int(size[qb]) * keys
+    return total * G
+
+
 def pyramid_bytes(p, nodes):
     elt = 2 if p.dtype == "bf16" else 4
     return p.batch * p.heads_kv * p.seq_len * p.head_dim * elt + p.batch * p.heads_kv * nodes * p.head_dim * 4
@@ -333,6 +353,49 @@ def run_prefill(args, dev):
         },
     }
 
+    if args.variants:
+        # the variants on the same inputs: bidirectional (mean summaries) and
+        # causal with max-pooled summaries; one step = pyramid, selection, attention
+        result["variants"] = {}
+        for name, causal, pool in (("bidirectional", 0, "mean"), ("max_pool", 1, "max")):
+            vp = pisa.problem(p.batch, p.heads_q, p.heads_kv, p.seq_len, p.head_dim, p.block_size, p.fanout,
+                              p.levels, p.top_k, p.sink_len, p.dtype, causal=causal, pool=pool)
+
+            def vstep(ev=None):
+                if ev is not None:
+                    ev[0].record()
+                pisa.build_pyramid(vp, k, pyr)
+                pisa.select_topk(vp, q, pyr, idx, cnt)
+                if ev is not None:
+                    ev[1].record()
+                pisa.sparse_attn_fwd(vp, q, k, v, idx, cnt, out)
+                if ev is not None:
+                    ev[2].record()
+
+            for _ in range(args.warmup):
+                vstep()
+            torch.cuda.synchronize()
+            ve = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.variant_steps)]
+            for e in ve:
+                vstep(e)
+            torch.cuda.synchronize()
+            t_ps = float(np.mean([e[0].elapsed_time(e[1]) for e in ve])) * 1e-3
+            t_at = float(np.mean([e[1].elapsed_time(e[2]) for e in ve])) * 1e-3
+            ih, ch = idx.cpu().numpy(), cnt.cpu().numpy()
+            vpairs = attended_pairs(p, ih, ch) if causal else attended_pairs_bidirectional(p, ih, ch)
+            vfl = 4.0 * p.head_dim * vpairs
+            log(f"variant {name}: {(t_ps + t_at) * 1e3:.3f} ms/step (pyramid+select {t_ps * 1e3:.3f} ms, "
+                f"attention {t_at * 1e3:.3f} ms, {vfl / t_at / 1e12:.1f} TFLOP/s)")
+            result["variants"][name] = {
+                "causal": bool(causal), "pool": pool,
+                "ms_per_step": (t_ps + t_at) * 1e3,
+                "tokens_per_s": p.batch * p.seq_len / (t_ps + t_at),
+                "pyramid_select_ms": t_ps * 1e3,
+                "attention_ms": t_at * 1e3,
+                "attention_TFLOP/s": vfl / t_at / 1e12,
+                "attention_frac": vfl / t_at / BF16_PEAK,
+            }
+
     if args.backward:
         # backward of the same attention: the forward's output and lse, an output
         # gradient, then dq, dk, dv (selection held constant)
@@ -496,6 +559,10 @@ def main(argv=None):
                     help="also time the backward pass on the prefill workload (default)")
     ap.add_argument("--no-backward", dest="backward", action="store_false")
     ap.add_argument("--backward-steps", type=int, default=5)
+    ap.add_argument("--variants", dest="variants", action="store_true", default=True,
+                    help="also time the bidirectional and max-pool variants on the prefill workload (default)")
+    ap.add_argument("--no-variants", dest="variants", action="store_false")
+    ap.add_argument("--variant-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args(argv)

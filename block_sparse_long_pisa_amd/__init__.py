@@ -18,6 +18,8 @@ __all__ = [
     "Problem",
     "F32",
     "BF16",
+    "POOL_MEAN",
+    "POOL_MAX",
     "EXPORTED_SYMBOLS",
     "library_path",
     "load_library",
@@ -78,6 +80,7 @@ class Problem(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("pool", ctypes.c_int32),
     ]
 
     @property
@@ -89,11 +92,15 @@ class Problem(ctypes.Structure):
         return self.heads_q // self.heads_kv
 
 
+POOL_MEAN, POOL_MAX = 0, 1
+
+
 def problem(batch, heads_q, heads_kv, seq_len, head_dim, block_size, fanout, levels, top_k, sink_len, dtype,
-            sm_scale=0.0, causal=1) -> Problem:
+            sm_scale=0.0, causal=1, pool=POOL_MEAN) -> Problem:
     d = {"f32": F32, "bf16": BF16}.get(dtype, dtype)
-    return Problem(batch, heads_q, heads_kv, head_dim, seq_len, block_size, fanout, levels, top_k, sink_len, causal,
-                   sm_scale, d)
+    pl = {"mean": POOL_MEAN, "max": POOL_MAX}.get(pool, pool)
+    return Problem(batch, heads_q, heads_kv, head_dim, seq_len, block_size, fanout, levels, top_k, sink_len,
+                   int(causal), sm_scale, d, pl)
 
 
 # ---------------------------------------------------------------------------

@@ -52,7 +52,8 @@ pisa_status make_geo(const pisa_problem* p, pisa::Geo* g) {
     return fail(PISA_ERR_UNSUPPORTED, "top_k * fanout + fanout - 1 = %d exceeds the %d-node pool",
                 p->top_k * p->fanout + p->fanout - 1, pisa::kPoolMax);
   if (p->sink_len < 0) return fail(PISA_ERR_SHAPE, "sink_len %d < 0", p->sink_len);
-  if (p->causal != 1) return fail(PISA_ERR_UNSUPPORTED, "causal %d: only causal attention is implemented", p->causal);
+  if (p->causal != 0 && p->causal != 1) return fail(PISA_ERR_UNSUPPORTED, "causal %d (0 or 1)", p->causal);
+  if (p->pool != PISA_POOL_MEAN && p->pool != PISA_POOL_MAX) return fail(PISA_ERR_UNSUPPORTED, "pool %d", p->pool);
   if (!(p->sm_scale == p->sm_scale)) return fail(PISA_ERR_SHAPE, "sm_scale is NaN");
   if (p->seq_len > (int64_t)INT32_MAX - 256) return fail(PISA_ERR_SHAPE, "seq_len %lld too large", (long long)p->seq_len);
   if ((int64_t)p->batch * p->heads_kv > 65535 || (int64_t)p->batch * p->heads_q > INT32_MAX)
@@ -73,6 +74,8 @@ pisa_status make_geo(const pisa_problem* p, pisa::Geo* g) {
   G.sink = p->sink_len;
   G.j0 = p->sink_len / p->block_size;
   G.dtype = p->dtype;
+  G.causal = p->causal;
+  G.pool = p->pool;
   G.scale = p->sm_scale > 0.f ? p->sm_scale : 1.0f / sqrtf((float)p->head_dim);
   int n = G.nb;
   int span = 1;
@@ -103,6 +106,7 @@ pisa_status check_decode(const pisa::Geo& g, const void* q, const void* k_cache,
                          const float* pyramid, const void* out, const void* workspace, size_t workspace_bytes) {
   if (g.G != 1 && g.G != 2 && g.G != 4 && g.G != 8)
     return fail(PISA_ERR_UNSUPPORTED, "decode supports 1, 2, 4 or 8 query heads per kv head (got %d)", g.G);
+  if (!g.causal) return fail(PISA_ERR_UNSUPPORTED, "decode is causal: the problem must have causal = 1");
   if (g.N < 1) return fail(PISA_ERR_SHAPE, "seq_len (the cache capacity) must be >= 1");
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || pyramid == nullptr || out == nullptr)
     return fail(PISA_ERR_NULL, "q, k_cache, v_cache, pyramid or out is NULL");
@@ -201,6 +205,7 @@ pisa_status pisa_sparse_attn_bwd(const pisa_problem* p, const void* q, const voi
   if (s != PISA_OK) return s;
   if (empty(g)) return ok();
   if (g.dtype != PISA_BF16) return fail(PISA_ERR_UNSUPPORTED, "the backward pass is implemented for bf16 only");
+  if (!g.causal) return fail(PISA_ERR_UNSUPPORTED, "the backward pass is implemented for causal attention only");
   if (q == nullptr || k == nullptr || v == nullptr || cnt == nullptr || out == nullptr || lse == nullptr ||
       dout == nullptr || dq == nullptr || dk == nullptr || dv == nullptr || (idx == nullptr && g.K > 0))
     return fail(PISA_ERR_NULL, "q, k, v, idx, cnt, out, lse, dout, dq, dk or dv is NULL");

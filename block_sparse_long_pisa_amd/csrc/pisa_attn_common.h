@@ -6,6 +6,8 @@
 // take from them.
 #pragma once
 
+#include <limits.h>
+
 #include "pisa_internal.h"
 
 namespace pisa {
@@ -34,39 +36,55 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // Which key block a tile index refers to, and how many of its keys count.
+// Causal walk of query block qb: the sink blocks before qb, the partial sink
+// block (unless selected), the selected blocks, the local block under the
+// causal mask. Bidirectional walk: every full sink block but qb, the partial
+// sink block (unless selected or qb), the selected blocks, the whole local block.
 struct TileWalk {
-  int nfull_sink;    // blocks wholly inside the sink (before qb)
-  int partial;       // 1 if the block holding the sink's end is attended as a sink tile
-  int nsel;          // selected blocks
-  int ntiles;        // + 1 local block
+  int nfull_sink;  // sink blocks attended whole
+  int skip;        // the sink block index the walk steps over (qb, bidirectional), else INT_MAX
+  int partial;     // 1 if the block holding the sink's end is attended as a sink tile
+  int nsel;        // selected blocks
+  int ntiles;      // + 1 local block
+  bool causal;
   __device__ __forceinline__ void at(int t, const int* sel, const Geo& g, int qb, int local_rows, int& j, int& nvalid,
                                      bool& local) const {
     local = false;
     if (t < nfull_sink) {
-      j = t;
-      nvalid = g.bs;
+      j = t + (t >= skip ? 1 : 0);
+      nvalid = min(g.bs, g.N - j * g.bs);
     } else if (t < nfull_sink + partial) {
       j = g.j0;
-      nvalid = g.sink - g.j0 * g.bs;
+      nvalid = min(g.sink, g.N) - g.j0 * g.bs;
     } else if (t < ntiles - 1) {
       j = sel[t - nfull_sink - partial];
-      nvalid = g.bs;
-      if (j < 0 || j >= qb) {  // not a block this unit may select: attend nothing from it
+      nvalid = min(g.bs, g.N - j * g.bs);
+      if (j < 0 || j >= (causal ? qb : g.nb) || j == qb) {  // not a block this unit may select: attend nothing
         j = qb;
         nvalid = 0;
       }
     } else {
       j = qb;
       nvalid = local_rows;
-      local = true;
+      local = causal;
     }
   }
 };
 
 __device__ __forceinline__ TileWalk make_walk(const Geo& g, int qb, const int* sel, int nsel) {
   TileWalk w;
-  w.nfull_sink = min(g.j0, qb);
-  const bool sink_tail = g.sink > g.j0 * g.bs && g.j0 < qb;
+  w.causal = g.causal != 0;
+  bool sink_tail;
+  if (w.causal) {
+    w.nfull_sink = min(g.j0, qb);
+    w.skip = INT_MAX;
+    sink_tail = g.sink > g.j0 * g.bs && g.j0 < qb;
+  } else {
+    const int jn = min(g.j0, g.nb);
+    w.nfull_sink = jn - (qb < jn ? 1 : 0);
+    w.skip = qb < jn ? qb : INT_MAX;
+    sink_tail = g.sink > g.j0 * g.bs && g.j0 < g.nb && g.j0 != qb;
+  }
   w.partial = (sink_tail && !(nsel > 0 && sel[0] == g.j0)) ? 1 : 0;
   w.nsel = nsel;
   w.ntiles = w.nfull_sink + w.partial + nsel + 1;

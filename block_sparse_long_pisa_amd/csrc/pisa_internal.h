@@ -21,6 +21,8 @@ struct Geo {
   int f, L, K;  // fanout, levels, top-k
   int sink, j0; // sink tokens; blocks wholly inside the sink
   int dtype;
+  int causal;   // 1: causal; 0: the bidirectional variant
+  int pool;     // PISA_POOL_MEAN or PISA_POOL_MAX
   int nodes[kMaxLevels];
   int off[kMaxLevels + 1];  // off[L] = nodes per slab
   int span[kMaxLevels];     // blocks under one node of level l (f^l)

@@ -1,4 +1,4 @@
-// Key pyramid by mean pooling ("Attention clairsemée PISA : noyaux Triton sans
+// Key pyramid by pooling -- the mean, or the element-wise maximum as a variant ("Attention clairsemée PISA : noyaux Triton sans
 // matrice de scores", sections "Une pyramide de clés plutôt qu'un tapis
 // uniforme" and "Le pooling comme première réduction").
 //
@@ -7,6 +7,8 @@
 // wave reduces whole blocks with 16-byte loads and fp64 accumulators, and the
 // workgroup folds its blocks' stored fp32 summaries into the level-1 node.
 // Coarser levels are tiny and fold from the level below in one launch each.
+#include <type_traits>
+
 #include "pisa_internal.h"
 
 namespace pisa {
@@ -16,9 +18,38 @@ constexpr int kPoolThreads = 256;
 constexpr int kUnroll = 8;
 constexpr int kMaxChunk = 16;  // blocks per workgroup (fanout <= 16)
 
-template <typename T, int D>
+// Summary arithmetic: the mean (fp64 sums, one rounding) or the element-wise
+// maximum (exact).
+template <bool MX>
+struct Pool {
+  using Acc = typename std::conditional<MX, float, double>::type;
+  __device__ __forceinline__ static Acc init() { return MX ? (Acc)-__builtin_inff() : (Acc)0; }
+  __device__ __forceinline__ static Acc add(Acc a, float x) {
+    if constexpr (MX) return fmaxf(a, x);
+    else return a + (double)x;
+  }
+  // a row read from a clamped address (past the block) repeats the last row:
+  // harmless for the maximum, left out of the sum
+  __device__ __forceinline__ static Acc add_row(Acc a, float x, bool real) {
+    if constexpr (MX) return fmaxf(a, x);
+    else return a + (real ? (double)x : 0.0);
+  }
+  __device__ __forceinline__ static Acc join(Acc a, Acc b) {
+    if constexpr (MX) return fmaxf(a, b);
+    else return a + b;
+  }
+  // summary of `count` folded values; for a power-of-two count the multiply by
+  // its reciprocal is the exact quotient
+  __device__ __forceinline__ static float fin(Acc a, int count) {
+    if constexpr (MX) return a;
+    else return (float)((count & (count - 1)) == 0 ? a * (1.0 / (double)count) : a / (double)count);
+  }
+};
+
+template <typename T, int D, bool MX>
 __global__ __launch_bounds__(kPoolThreads) void pool_leaf_kernel(Geo g, const T* __restrict__ k,
                                                                   float* __restrict__ pyr, int chunk_blocks) {
+  using PO = Pool<MX>;
   constexpr int VEC = Wide<T>::kVec;
   constexpr int LPR = D / VEC;   // lanes covering one key row
   constexpr int RPI = 64 / LPR;  // rows one wave instruction covers
@@ -38,9 +69,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_leaf_kernel(Geo g, const T*
     const int j = j_first + jj;
     const int r0 = j * g.bs;
     const int r1 = min(g.N, r0 + g.bs);
-    double acc[VEC];
+    typename PO::Acc acc[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+    for (int e = 0; e < VEC; ++e) acc[e] = PO::init();
     for (int r = r0 + rsub; r < r1; r += RPI * kUnroll) {
       uint4 raw[kUnroll];
 #pragma unroll
@@ -51,23 +82,20 @@ __global__ __launch_bounds__(kPoolThreads) void pool_leaf_kernel(Geo g, const T*
         float x[VEC];
         Wide<T>::widen(raw[u], x);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += r + u * RPI < r1 ? (double)x[e] : 0.0;
+        for (int e = 0; e < VEC; ++e) acc[e] = PO::add_row(acc[e], x[e], r + u * RPI < r1);
       }
     }
-    // sum the row slots that share these columns
+    // fold the row slots that share these columns
 #pragma unroll
     for (int s = LPR; s < 64; s <<= 1)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], s);
+      for (int e = 0; e < VEC; ++e) acc[e] = PO::join(acc[e], __shfl_xor(acc[e], s));
     if (rsub == 0) {
-      const double inv_cnt = 1.0 / (double)(r1 - r0);
       float outv[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        // bs is a power of two, so the multiply is exact for full blocks; a
-        // partial last block divides by its row count
-        const double mean = ((r1 - r0) == g.bs) ? acc[e] * inv_cnt : acc[e] / (double)(r1 - r0);
-        outv[e] = (float)mean;
+        // the mean divides by the row count (a power of two for full blocks, exact)
+        outv[e] = PO::fin(acc[e], r1 - r0);
         leaf[jj][col + e] = outv[e];
       }
       float* dst = pb + (int64_t)j * D + col;
@@ -78,23 +106,24 @@ __global__ __launch_bounds__(kPoolThreads) void pool_leaf_kernel(Geo g, const T*
   if (g.L < 2) return;
   __syncthreads();
   for (int c = threadIdx.x; c < D; c += kPoolThreads) {
-    double s = 0.0;
-    for (int jj = 0; jj < nblk; ++jj) s += (double)leaf[jj][c];
-    pb[(int64_t)(g.off[1] + blockIdx.x) * D + c] = (float)(s / (double)nblk);
+    typename PO::Acc s = PO::init();
+    for (int jj = 0; jj < nblk; ++jj) s = PO::add(s, leaf[jj][c]);
+    pb[(int64_t)(g.off[1] + blockIdx.x) * D + c] = PO::fin(s, nblk);
   }
 }
 
 // One coarse level: node n of level l = mean of its children at level l - 1.
-template <int D>
+template <int D, bool MX>
 __global__ __launch_bounds__(D) void pool_coarse_kernel(Geo g, float* __restrict__ pyr, int l) {
+  using PO = Pool<MX>;
   const int n = blockIdx.x;
   const int slab = blockIdx.y;
   float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
   const int c0 = n * g.f;
   const int c1 = min(c0 + g.f, g.nodes[l - 1]);
-  double s = 0.0;
-  for (int c = c0; c < c1; ++c) s += (double)pb[(int64_t)(g.off[l - 1] + c) * D + threadIdx.x];
-  pb[(int64_t)(g.off[l] + n) * D + threadIdx.x] = (float)(s / (double)(c1 - c0));
+  typename PO::Acc s = PO::init();
+  for (int c = c0; c < c1; ++c) s = PO::add(s, pb[(int64_t)(g.off[l - 1] + c) * D + threadIdx.x]);
+  pb[(int64_t)(g.off[l] + n) * D + threadIdx.x] = PO::fin(s, c1 - c0);
 }
 
 // Update after an append: tokens [len0, len1) of sequence b were written to the
@@ -104,11 +133,12 @@ __global__ __launch_bounds__(D) void pool_coarse_kernel(Geo g, float* __restrict
 // one built over the first len1 tokens. Nodes before len0 are untouched. One
 // workgroup per (batch, kv head); a decode step's append touches one leaf and
 // one node per coarser level.
-template <typename T, int D>
+template <typename T, int D, bool MX>
 __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const T* __restrict__ k,
                                                                    float* __restrict__ pyr,
                                                                    const int32_t* __restrict__ old_lens,
                                                                    const int32_t* __restrict__ new_lens) {
+  using PO = Pool<MX>;
   constexpr int VEC = Wide<T>::kVec;
   constexpr int LPR = D / VEC;
   constexpr int RPI = 64 / LPR;
@@ -127,9 +157,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
   for (int j = a + wave; j <= z; j += kPoolThreads / 64) {
     const int r0 = j * g.bs;
     const int r1 = min(len1, r0 + g.bs);
-    double acc[VEC];
+    typename PO::Acc acc[VEC];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+    for (int e = 0; e < VEC; ++e) acc[e] = PO::init();
     for (int r = r0 + rsub; r < r1; r += RPI * kUnroll) {
       uint4 raw[kUnroll];
 #pragma unroll
@@ -139,16 +169,16 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
         float x[VEC];
         Wide<T>::widen(raw[u], x);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] += r + u * RPI < r1 ? (double)x[e] : 0.0;
+        for (int e = 0; e < VEC; ++e) acc[e] = PO::add_row(acc[e], x[e], r + u * RPI < r1);
       }
     }
 #pragma unroll
     for (int sh = LPR; sh < 64; sh <<= 1)
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += __shfl_xor(acc[e], sh);
+      for (int e = 0; e < VEC; ++e) acc[e] = PO::join(acc[e], __shfl_xor(acc[e], sh));
     if (rsub == 0) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) pb[(int64_t)j * D + col + e] = (float)(acc[e] / (double)(r1 - r0));
+      for (int e = 0; e < VEC; ++e) pb[(int64_t)j * D + col + e] = PO::fin(acc[e], r1 - r0);
     }
   }
   __syncthreads();
@@ -159,9 +189,9 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
       const int n = na + e / D, c = e % D;
       const int c0 = n * g.f;
       const int c1 = min(c0 + g.f, present);
-      double sum = 0.0;
-      for (int ch = c0; ch < c1; ++ch) sum += (double)pb[(int64_t)(g.off[l - 1] + ch) * D + c];
-      pb[(int64_t)(g.off[l] + n) * D + c] = (float)(sum / (double)(c1 - c0));
+      typename PO::Acc sum = PO::init();
+      for (int ch = c0; ch < c1; ++ch) sum = PO::add(sum, pb[(int64_t)(g.off[l - 1] + ch) * D + c]);
+      pb[(int64_t)(g.off[l] + n) * D + c] = PO::fin(sum, c1 - c0);
     }
     __syncthreads();
     a = na;
@@ -170,28 +200,40 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
   }
 }
 
-template <typename T, int D>
-hipError_t launch_append_t(const Geo& g, const void* k, float* pyr, const int32_t* old_lens, const int32_t* new_lens,
+template <typename T, int D, bool MX>
+hipError_t launch_append_m(const Geo& g, const void* k, float* pyr, const int32_t* old_lens, const int32_t* new_lens,
                            hipStream_t s) {
-  hipLaunchKernelGGL((pool_append_kernel<T, D>), dim3(g.B * g.Hkv), dim3(kPoolThreads), 0, s, g, (const T*)k, pyr,
+  hipLaunchKernelGGL((pool_append_kernel<T, D, MX>), dim3(g.B * g.Hkv), dim3(kPoolThreads), 0, s, g, (const T*)k, pyr,
                      old_lens, new_lens);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_pool_t(const Geo& g, const void* k, float* pyr, hipStream_t s) {
+hipError_t launch_append_t(const Geo& g, const void* k, float* pyr, const int32_t* old_lens, const int32_t* new_lens,
+                           hipStream_t s) {
+  return g.pool == PISA_POOL_MAX ? launch_append_m<T, D, true>(g, k, pyr, old_lens, new_lens, s)
+                                 : launch_append_m<T, D, false>(g, k, pyr, old_lens, new_lens, s);
+}
+
+template <typename T, int D, bool MX>
+hipError_t launch_pool_m(const Geo& g, const void* k, float* pyr, hipStream_t s) {
   const int slabs = g.B * g.Hkv;
   const int chunk = g.L >= 2 ? g.f : 8;
   dim3 grid((g.nb + chunk - 1) / chunk, slabs);
-  hipLaunchKernelGGL((pool_leaf_kernel<T, D>), grid, dim3(kPoolThreads), 0, s, g, (const T*)k, pyr, chunk);
+  hipLaunchKernelGGL((pool_leaf_kernel<T, D, MX>), grid, dim3(kPoolThreads), 0, s, g, (const T*)k, pyr, chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   for (int l = 2; l < g.L; ++l) {
-    hipLaunchKernelGGL((pool_coarse_kernel<D>), dim3(g.nodes[l], slabs), dim3(D), 0, s, g, pyr, l);
+    hipLaunchKernelGGL((pool_coarse_kernel<D, MX>), dim3(g.nodes[l], slabs), dim3(D), 0, s, g, pyr, l);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+template <typename T, int D>
+hipError_t launch_pool_t(const Geo& g, const void* k, float* pyr, hipStream_t s) {
+  return g.pool == PISA_POOL_MAX ? launch_pool_m<T, D, true>(g, k, pyr, s) : launch_pool_m<T, D, false>(g, k, pyr, s);
 }
 
 }  // namespace

@@ -126,6 +126,18 @@ __device__ __forceinline__ double row16_sum(double v) {
   return v;
 }
 
+// Is node n of level l a candidate node for query block qb? Causal: it holds a
+// block outside the sink (pools only ever hold complete nodes before the query
+// block's ancestor); bidirectional: it exists and holds a block outside the sink
+// other than qb itself.
+__device__ __forceinline__ bool node_ok(const Geo& g, int l, int n, int qb, int lo) {
+  if (g.causal) return n >= lo;
+  if (n >= g.nodes[l]) return false;
+  const int a = max(n * g.span[l], g.j0);
+  const int b = min((n + 1) * g.span[l], g.nb);
+  return b - a - ((a <= qb && qb < b) ? 1 : 0) > 0;
+}
+
 // Node id held by pool slot p at level l (kept children first, then the
 // complete children of the query block's own ancestor).
 __device__ __forceinline__ int slot_node(int p, int nchild, int f, const int* kept, int anc_first) {
@@ -135,9 +147,9 @@ __device__ __forceinline__ int slot_node(int p, int nchild, int f, const int* ke
 // Score pool slots [0, M) into sm.sc (fp64 dot products with the query mean).
 // 16 lanes per node, four nodes per wave instruction, four instructions in flight.
 template <int E, int D, int NWS>
-__device__ __forceinline__ void score_slots(const float* __restrict__ lvl, int M, int nchild, int f, int anc_first,
-                                            int lo, WaveSmem<E, D>& sm, const double (&qv)[D / 16], int lane,
-                                            int wave) {
+__device__ __forceinline__ void score_slots(const Geo& g, int l, int qb, const float* __restrict__ lvl, int M,
+                                            int nchild, int f, int anc_first, int lo, WaveSmem<E, D>& sm,
+                                            const double (&qv)[D / 16], int lane, int wave) {
   constexpr int DPL = D / 16;
   constexpr int U = 8;
   const int grp = wave * 4 + (lane >> 4);  // 16-lane group among the NWS cooperating waves
@@ -149,7 +161,7 @@ __device__ __forceinline__ void score_slots(const float* __restrict__ lvl, int M
     for (int u = 0; u < U; ++u) {
       const int p = base + u * 4 * NWS + grp;
       const int n = p < M ? slot_node(p, nchild, f, sm.kept, anc_first) : 0;
-      use[u] = p < M && n >= lo;
+      use[u] = p < M && node_ok(g, l, n, qb, lo);
       // unused slots read node 0 (always present) so that no load is conditional
       const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)(use[u] ? n : 0) * D + sub * DPL);
 #pragma unroll
@@ -199,11 +211,25 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
 #pragma unroll
   for (int e = 0; e < DPL; ++e) qv[e] = sm.qbar[(lane & 15) * DPL + e];
   const int L = g.L;
-  // top level: complete nodes before the ancestor that hold a non-sink block
+  // top level: causal -- the complete nodes before the ancestor that hold a
+  // non-sink block; bidirectional -- every node holding a candidate
   int lo = g.j0 / g.span[L - 1];
-  int M = max(0, qb / g.span[L - 1] - lo);
-  int nchild = 0;      // slots that are children of kept nodes
-  int anc_first = lo;  // first node of the contiguous tail of the pool
+  int M = g.causal ? max(0, qb / g.span[L - 1] - lo) : g.nodes[L - 1];
+  int nchild = 0;                      // slots that are children of kept nodes
+  int anc_first = g.causal ? lo : 0;   // first node of the contiguous tail of the pool
+  // next level's pool: children of the kept nodes, then (causal) the complete
+  // children of the ancestor; invalid nodes are masked by node_ok
+  auto next_pool = [&](int l, int nk) {
+    nchild = nk * g.f;
+    if (g.causal) {
+      anc_first = (qb / g.span[l]) * g.f;
+      M = nchild + (qb / g.span[l - 1] - anc_first);
+    } else {
+      anc_first = 0;
+      M = nchild;
+    }
+    lo = g.j0 / g.span[l - 1];
+  };
   for (int l = L - 1; l >= 0; --l) {
     // slot ids and validity need no scores
     int id[E];
@@ -212,24 +238,21 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
     for (int e = 0; e < E; ++e) {
       const int p = e * 64 + lane;
       const int n = p < M ? slot_node(p, nchild, g.f, sm.kept, anc_first) : INT_MAX;
-      const bool valid = p < M && n >= lo;
+      const bool valid = p < M && node_ok(g, l, n, qb, lo);
       id[e] = valid ? n : INT_MAX;
       nvalid += __popcll(__ballot(valid));
     }
     const int nk = min(g.K, nvalid);
     const bool ranked = nvalid > g.K;  // uniform across the cooperating waves
     if (ranked) {
-      score_slots<E, D, NWS>(ps + (int64_t)g.off[l] * D, M, nchild, g.f, anc_first, lo, sm, qv, lane, wave);
+      score_slots<E, D, NWS>(g, l, qb, ps + (int64_t)g.off[l] * D, M, nchild, g.f, anc_first, lo, sm, qv, lane,
+                             wave);
       sync_scorers<NWS>();
     }
     if (NWS > 1 && wave != 0) {  // helpers: wait for wave 0's kept list, then go on
       if (l == 0) return;
       sync_scorers<NWS>();
-      const int a_l = qb / g.span[l];
-      nchild = nk * g.f;
-      anc_first = a_l * g.f;
-      M = nchild + (qb / g.span[l - 1] - anc_first);
-      lo = g.j0 / g.span[l - 1];
+      next_pool(l, nk);
       continue;
     }
     if (ranked) {
@@ -263,13 +286,7 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
       return;
     }
     sync_scorers<NWS>();
-    // next level's pool: children of the kept nodes, then the complete children
-    // of the ancestor; nodes wholly inside the sink are invalid
-    const int a_l = qb / g.span[l];
-    nchild = nk * g.f;
-    anc_first = a_l * g.f;
-    M = nchild + (qb / g.span[l - 1] - anc_first);
-    lo = g.j0 / g.span[l - 1];
+    next_pool(l, nk);
   }
 }
 

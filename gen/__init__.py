@@ -68,6 +68,8 @@ class Problem:
     dtype: str  # "f32" or "bf16"
     sm_scale: float = 0.0  # <= 0 means 1/sqrt(head_dim)
     decode: bool = False
+    causal: bool = True    # False: the bidirectional variant
+    pool: str = "mean"     # "mean", or the "max" variant of node summaries
 
     @property
     def group(self) -> int:

@@ -59,6 +59,11 @@ typedef enum pisa_status {
 
 typedef enum pisa_dtype { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
 
+/* How a pyramid node summarises its keys ("Le pooling comme première
+ * réduction" names pooling without fixing the operator): the mean (the method's
+ * default reading) or, as a variant, the element-wise maximum. */
+typedef enum pisa_pool { PISA_POOL_MEAN = 0, PISA_POOL_MAX = 1 } pisa_pool;
+
 /* Problem description, passed by const pointer to every call.
  *   heads_q % heads_kv == 0; the G = heads_q / heads_kv query heads of one KV
  *     head share one selection (grouped-query attention).
@@ -70,9 +75,14 @@ typedef enum pisa_dtype { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype;
  *     1024 nodes and top_k * fanout + fanout - 1 <= 1024.
  *   top_k: >= 0 key blocks kept per query block (the beam width at every level).
  *   sink_len: >= 0 tokens of the always-attended prefix [0, sink_len).
- *   causal: must be 1 (0 returns PISA_ERR_UNSUPPORTED).
+ *   causal: 1, or 0 for the bidirectional variant: every block outside the
+ *     sink except the query block's own is a candidate, the descent scores
+ *     every node holding a candidate, and the query block is attended whole.
+ *     Selection and the forward attention take 0; decode and the backward pass
+ *     return PISA_ERR_UNSUPPORTED for it.
  *   sm_scale: softmax scale; <= 0 selects 1/sqrt(head_dim).
- *   dtype: PISA_F32 or PISA_BF16 for Q, K, V and O. */
+ *   dtype: PISA_F32 or PISA_BF16 for Q, K, V and O.
+ *   pool: PISA_POOL_MEAN or PISA_POOL_MAX (node summaries of the pyramid). */
 typedef struct pisa_problem {
   int32_t batch;
   int32_t heads_q;
@@ -87,6 +97,7 @@ typedef struct pisa_problem {
   int32_t causal;
   float sm_scale;
   int32_t dtype;
+  int32_t pool;
 } pisa_problem;
 
 /* Node offsets of each pyramid level ("Une pyramide de clés"). Host only, pure.

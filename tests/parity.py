@@ -26,7 +26,7 @@ def log(msg: str):
 
 def cprob(p: gen.Problem):
     return pisa.problem(p.batch, p.heads_q, p.heads_kv, p.seq_len, p.head_dim, p.block_size, p.fanout, p.levels,
-                        p.top_k, p.sink_len, p.dtype, sm_scale=p.sm_scale)
+                        p.top_k, p.sink_len, p.dtype, sm_scale=p.sm_scale, causal=int(p.causal), pool=p.pool)
 
 
 def to_dev(x: np.ndarray, dtype: str):
@@ -58,10 +58,14 @@ def gpu_prefill(p: gen.Problem, q, k, v, want_lse=True):
 
 
 def oracle_select(p: gen.Problem, q: np.ndarray, k: np.ndarray):
-    pyr = oracle.build_pyramid(k, p.block_size, p.fanout, p.levels)
+    pyr = oracle.build_pyramid(k, p.block_size, p.fanout, p.levels, pool=p.pool)
     qbar = oracle.query_block_means(q, p.heads_kv, p.block_size)
-    idx, cnt = oracle.select(pyr, qbar, p.top_k, p.sink_len, p.block_size, p.fanout)
+    idx, cnt = oracle.select(pyr, qbar, p.top_k, p.sink_len, p.block_size, p.fanout, causal=p.causal)
     return pyr, idx, cnt
+
+
+def oracle_attend(p: gen.Problem, q, k, v, idx, cnt, blocks=None):
+    return oracle.attend(q, k, v, idx, cnt, p.sink_len, p.block_size, p.scale, blocks=blocks, causal=p.causal)
 
 
 def assert_pyramid_equal(gpu_levels, ora_levels):

@@ -35,10 +35,15 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_struct_layout_matches_header():
-    # int32 x4, int64, int32 x6, float, int32 -> 56 bytes with the int64 at offset 16
-    assert ctypes.sizeof(pisa.Problem) == 56
+    # int32 x4, int64, int32 x6, float, int32 x2 -> 60 bytes padded to 64 (int64 alignment)
+    assert ctypes.sizeof(pisa.Problem) == 64
     assert pisa.Problem.seq_len.offset == 16
     assert pisa.Problem.dtype.offset == 52
+    assert pisa.Problem.pool.offset == 56
+    fields = re.search(r"typedef struct pisa_problem \{(.*?)\} pisa_problem;", open(os.path.join(ROOT, "include", "pisa.h")).read(),
+                       re.S).group(1)
+    names = re.findall(r"(?:int32_t|int64_t|float)\s+(\w+);", fields)
+    assert names == [f[0] for f in pisa.Problem._fields_]
 
 
 def _p(**kw):
@@ -69,7 +74,8 @@ def test_layout_offsets(lib):
     (dict(top_k=300), EUNSUP),
     (dict(top_k=128, fanout=16), EUNSUP),
     (dict(sink_len=-1), ESHAPE),
-    (dict(causal=0), EUNSUP),
+    (dict(causal=2), EUNSUP),
+    (dict(pool=2), EUNSUP),
     (dict(dtype=7), EUNSUP),
     (dict(seq_len=1 << 20, block_size=32, levels=1), EUNSUP),  # top level too wide
 ])

@@ -41,3 +41,18 @@ def test_append_bytes_single_token_by_hand():
     want = p.heads_kv * (rows * p.head_dim * 2 + (read + written) * p.head_dim * 4)
     assert bench.append_bytes(p, [1000], [1001]) == want
     assert bench.append_bytes(p, [5], [5]) == 0 and bench.append_bytes(p, [-1], [3]) == 0
+
+
+def test_bidirectional_pairs_count_every_attended_key_once():
+    p = gen.Problem(1, 4, 2, 1000, 16, 32, 4, 3, 3, 40, "f32", causal=False)
+    q, k, v, _ = gen.host_inputs(p, 1, 1.0, ("uniform_pairs", 4))
+    pyr = oracle.build_pyramid(k, p.block_size, p.fanout, p.levels)
+    idx, cnt = oracle.select(pyr, oracle.query_block_means(q, p.heads_kv, p.block_size), p.top_k, p.sink_len,
+                             p.block_size, p.fanout, causal=False)
+    brute = 0
+    for g in range(p.heads_kv):
+        for i in range(p.seq_len):
+            qb = i // p.block_size
+            sel = idx[0, g, qb, :cnt[0, g, qb]].tolist()
+            brute += len(oracle.attended_keys(i, sel, p.sink_len, p.block_size, causal=False, n=p.seq_len))
+    assert bench.attended_pairs_bidirectional(p, idx, cnt) == brute * p.group
