@@ -6,7 +6,8 @@
 // over K: a workgroup owns one level-1 node (fanout consecutive blocks), each
 // wave reduces whole blocks with 16-byte loads and fp64 accumulators, and the
 // workgroup folds its blocks' stored fp32 summaries into the level-1 node.
-// Coarser levels are tiny and fold from the level below in one launch each.
+// Coarser levels are tiny: one more launch folds them all, a workgroup per
+// top-level node.
 #include <type_traits>
 
 #include "pisa_internal.h"
@@ -112,20 +113,6 @@ __global__ __launch_bounds__(kPoolThreads) void pool_leaf_kernel(Geo g, const T*
   }
 }
 
-// One coarse level: node n of level l = mean of its children at level l - 1.
-template <int D, bool MX>
-__global__ __launch_bounds__(D) void pool_coarse_kernel(Geo g, float* __restrict__ pyr, int l) {
-  using PO = Pool<MX>;
-  const int n = blockIdx.x;
-  const int slab = blockIdx.y;
-  float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
-  const int c0 = n * g.f;
-  const int c1 = min(c0 + g.f, g.nodes[l - 1]);
-  typename PO::Acc s = PO::init();
-  for (int c = c0; c < c1; ++c) s = PO::add(s, pb[(int64_t)(g.off[l - 1] + c) * D + threadIdx.x]);
-  pb[(int64_t)(g.off[l] + n) * D + threadIdx.x] = PO::fin(s, c1 - c0);
-}
-
 // Update after an append: tokens [len0, len1) of sequence b were written to the
 // key cache. Every node whose tokens meet [len0, len1) is recomputed over its
 // tokens before len1 -- leaves from the key rows, coarser nodes from the
@@ -200,6 +187,60 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
   }
 }
 
+// All levels from 2 up in one launch: a workgroup owns one top-level node and
+// builds its subtree level by level from the level-1 summaries. Within a level
+// each thread folds NM nodes of one column, and all F x NM child loads of a
+// round are issued before any is used.
+constexpr int kUpperThreads = 256;
+
+template <int D, bool MX, int F>
+__global__ __launch_bounds__(kUpperThreads) void pool_upper_kernel(Geo g, float* __restrict__ pyr) {
+  using PO = Pool<MX>;
+  constexpr int CPT = kUpperThreads / D;  // node groups per column
+  constexpr int NM = 64 / F;              // nodes a thread folds per round
+  const int top = blockIdx.x;
+  const int slab = blockIdx.y;
+  float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
+  const int c = threadIdx.x % D;
+  const int grp = threadIdx.x / D;
+  for (int l = 2; l < g.L; ++l) {
+    const int sub = g.span[g.L - 1] / g.span[l];  // level-l nodes under one top node
+    const int n0 = top * sub;
+    const int n1 = min(n0 + sub, g.nodes[l]);
+    const int below = g.nodes[l - 1];
+    for (int nb0 = n0 + grp * NM; nb0 < n1; nb0 += CPT * NM) {
+      float x[NM][F];
+#pragma unroll
+      for (int u = 0; u < NM; ++u)
+#pragma unroll
+        for (int ch = 0; ch < F; ++ch)  // clamped, unconditional loads
+          x[u][ch] = pb[(int64_t)(g.off[l - 1] + min((nb0 + u) * F + ch, below - 1)) * D + c];
+#pragma unroll
+      for (int u = 0; u < NM; ++u) {
+        const int n = nb0 + u;
+        const int cnt = min(F, below - n * F);  // children present (the last node may have fewer)
+        typename PO::Acc acc = PO::init();
+#pragma unroll
+        for (int ch = 0; ch < F; ++ch) acc = PO::add_row(acc, x[u][ch], ch < cnt);
+        if (n < n1) pb[(int64_t)(g.off[l] + n) * D + c] = PO::fin(acc, cnt);
+      }
+    }
+    __syncthreads();  // this level's summaries are read by the next
+  }
+}
+
+template <int D, bool MX>
+hipError_t launch_upper(const Geo& g, float* pyr, hipStream_t s) {
+  const dim3 grid(g.nodes[g.L - 1], g.B * g.Hkv);
+  switch (g.f) {
+    case 2: hipLaunchKernelGGL((pool_upper_kernel<D, MX, 2>), grid, dim3(kUpperThreads), 0, s, g, pyr); break;
+    case 4: hipLaunchKernelGGL((pool_upper_kernel<D, MX, 4>), grid, dim3(kUpperThreads), 0, s, g, pyr); break;
+    case 8: hipLaunchKernelGGL((pool_upper_kernel<D, MX, 8>), grid, dim3(kUpperThreads), 0, s, g, pyr); break;
+    default: hipLaunchKernelGGL((pool_upper_kernel<D, MX, 16>), grid, dim3(kUpperThreads), 0, s, g, pyr); break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool MX>
 hipError_t launch_append_m(const Geo& g, const void* k, float* pyr, const int32_t* old_lens, const int32_t* new_lens,
                            hipStream_t s) {
@@ -223,12 +264,8 @@ hipError_t launch_pool_m(const Geo& g, const void* k, float* pyr, hipStream_t s)
   hipLaunchKernelGGL((pool_leaf_kernel<T, D, MX>), grid, dim3(kPoolThreads), 0, s, g, (const T*)k, pyr, chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  for (int l = 2; l < g.L; ++l) {
-    hipLaunchKernelGGL((pool_coarse_kernel<D, MX>), dim3(g.nodes[l], slabs), dim3(D), 0, s, g, pyr, l);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  if (g.L < 3) return hipSuccess;
+  return launch_upper<D, MX>(g, pyr, s);
 }
 
 template <typename T, int D>
