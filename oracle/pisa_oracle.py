@@ -291,8 +291,13 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, cnt: np
 
 
 def attend_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, cnt: np.ndarray,
-                    dout: np.ndarray, sink_len: int, block_size: int, sm_scale: float):
+                    dout: np.ndarray, sink_len: int, block_size: int, sm_scale: float,
+                    units: Optional[Sequence] = None):
     """Gradients of L = sum(dout * o) for o = attend(q, k, v, idx, cnt), the selection held constant.
+
+    `units`, if given, is a list of (b, g, qb) query-block units whose terms are
+    summed (dq rows of other units stay 0; dk and dv then hold only these units'
+    contributions -- exact for a key block when every unit attending it is listed).
 
     Per query row i with attended keys A(i): s_t = sm_scale q_i.k_t, p = softmax_A(i)(s),
     o_i = sum_t p_t v_t. Then dv_t += p_t dout_i, dp_t = dout_i.v_t,
@@ -307,25 +312,24 @@ def attend_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray
     dq = np.zeros((B, Hq, N, d))
     dk = np.zeros((B, Hkv, N, d))
     dv = np.zeros((B, Hkv, N, d))
-    for b in range(B):
-        for g in range(Hkv):
-            kk, vv = k[b, g].astype(np.float64), v[b, g].astype(np.float64)
-            for qb in range(nb):
-                sel = idx[b, g, qb, :cnt[b, g, qb]].tolist()
-                r0, r1 = qb * block_size, min(N, (qb + 1) * block_size)
-                keys = attended_keys(r1 - 1, sel, sink_len, block_size)
-                pos = np.arange(r0, r1)[:, None]
-                for h in range(g * G, (g + 1) * G):
-                    qq = q[b, h, r0:r1].astype(np.float64)
-                    do = dout[b, h, r0:r1].astype(np.float64)
-                    s = sm_scale * (qq @ kk[keys].T)
-                    s = np.where(keys[None, :] <= pos, s, -np.inf)
-                    p, _ = _softmax_rows(s)
-                    dp = do @ vv[keys].T
-                    ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
-                    dq[b, h, r0:r1] = sm_scale * (ds @ kk[keys])
-                    np.add.at(dk[b, g], keys, sm_scale * (ds.T @ qq))
-                    np.add.at(dv[b, g], keys, p.T @ do)
+    todo = units if units is not None else [(b, g, qb) for b in range(B) for g in range(Hkv) for qb in range(nb)]
+    for (b, g, qb) in todo:
+        sel = idx[b, g, qb, :cnt[b, g, qb]].tolist()
+        r0, r1 = qb * block_size, min(N, (qb + 1) * block_size)
+        keys = attended_keys(r1 - 1, sel, sink_len, block_size)
+        kk, vv = k[b, g, keys].astype(np.float64), v[b, g, keys].astype(np.float64)
+        pos = np.arange(r0, r1)[:, None]
+        for h in range(g * G, (g + 1) * G):
+            qq = q[b, h, r0:r1].astype(np.float64)
+            do = dout[b, h, r0:r1].astype(np.float64)
+            s = sm_scale * (qq @ kk.T)
+            s = np.where(keys[None, :] <= pos, s, -np.inf)
+            p, _ = _softmax_rows(s)
+            dp = do @ vv.T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+            dq[b, h, r0:r1] = sm_scale * (ds @ kk)
+            np.add.at(dk[b, g], keys, sm_scale * (ds.T @ qq))
+            np.add.at(dv[b, g], keys, p.T @ do)
     return dq, dk, dv
 
 
