@@ -57,43 +57,59 @@ __device__ __forceinline__ uint64_t score_key(double s) {
 }
 
 // Keep the nk best of the wave's pool slots -- score descending, node index
-// ascending -- without sorting. key[e] is 0 for an empty slot, so only valid
-// slots (nk <= their count) are ever kept. The nk-th largest key T is found bit
-// by bit with wave-wide counts; every slot above T is kept, and of the slots at
-// T the lowest node indices fill the rest. Writes the kept node ids to kept[]
-// in slot order. All slots take part in every count (empty ones never reach a
-// threshold), so the counts stay scalar and branch-free.
+// ascending -- without sorting. Only slots e < ne can be in use (ne uniform);
+// key[e] is 0 for an empty slot, so only valid slots (nk <= their count) are
+// ever kept. A threshold is found bit by bit, most significant first, with
+// wave-wide counts of the keys at or above it. As soon as exactly nk keys lie at
+// or above the prefix found so far, those are the nk best and the search stops
+// (with distinct scores near the boundary this takes about as many bits as
+// separate the nk-th key from the next). Otherwise the search ends at T, the
+// nk-th largest key: every slot above T is kept, and of the slots at T the
+// lowest node indices fill the rest. Writes the kept node ids to kept[] in slot
+// order. Counts are scalar and branch-free within a step.
 template <int E>
-__device__ __forceinline__ void wave_keep_best(const uint64_t (&key)[E], const int (&id)[E], int nk, int* kept,
-                                               int lane) {
+__device__ __forceinline__ void wave_keep_best(const uint64_t (&key)[E], const int (&id)[E], int nk, int ne,
+                                               int* kept, int lane) {
   uint64_t T = 0;
+  bool exact = false;  // exactly nk keys are >= T
   for (int b = 63; b >= 0; --b) {
     const uint64_t cand = T | (1ull << b);
     int c = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
-    if (c >= nk) T = cand;
-  }
-  int above = 0, at = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    above += __popcll(__ballot(key[e] > T));
-    at += __popcll(__ballot(key[e] == T));
-  }
-  const int need = nk - above;  // >= 1 slots at T to keep
-  // when more slots tie at T than are needed, keep those with index <= I, the
-  // need-th smallest index among them (indices of valid slots are distinct)
-  int I = INT_MAX;
-  if (at > need) {
-    int lo = 0, hi = INT_MAX;  // smallest I with #{tied, id <= I} >= need
-    while (lo < hi) {
-      const int mid = lo + (hi - lo) / 2;
-      int c = 0;
-#pragma unroll
-      for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] == T && id[e] <= mid));
-      if (c >= need) hi = mid; else lo = mid + 1;
+    for (int e = 0; e < E; ++e)
+      if (e < ne) c += __popcll(__ballot(key[e] >= cand));
+    if (c >= nk) {
+      T = cand;
+      if (c == nk) {
+        exact = true;
+        break;
+      }
     }
-    I = lo;
+  }
+  int I = INT_MAX;  // keys at T are kept when their node index is <= I
+  if (!exact) {
+    int above = 0, at = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (e < ne) {
+        above += __popcll(__ballot(key[e] > T));
+        at += __popcll(__ballot(key[e] == T));
+      }
+    const int need = nk - above;  // >= 1 slots at T to keep
+    // when more slots tie at T than are needed, keep those with index <= I, the
+    // need-th smallest index among them (indices of valid slots are distinct)
+    if (at > need) {
+      int lo = 0, hi = INT_MAX;  // smallest I with #{tied, id <= I} >= need
+      while (lo < hi) {
+        const int mid = lo + (hi - lo) / 2;
+        int c = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (e < ne) c += __popcll(__ballot(key[e] == T && id[e] <= mid));
+        if (c >= need) hi = mid; else lo = mid + 1;
+      }
+      I = lo;
+    }
   }
   int base = 0;
 #pragma unroll
@@ -262,7 +278,7 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
         const int p = e * 64 + lane;
         key[e] = (p < M && id[e] != INT_MAX) ? score_key(sm.sc[p]) : 0ull;
       }
-      wave_keep_best<E>(key, id, nk, sm.kept, lane);
+      wave_keep_best<E>(key, id, nk, (M + 63) >> 6, sm.kept, lane);
     } else {
       // keep every valid slot, compacted in slot order
       int base = 0;
