@@ -17,36 +17,86 @@ namespace pisa {
 namespace {
 
 // Mean of the query block's rows over the group's heads (fp64), by one wave.
+// The unit's rows are G runs of `rows` consecutive rows, one run per head. A
+// lane covers VEC columns of every RPI-th row. Rounds of U loads are issued
+// before any is summed; full rounds run unmasked and one masked round takes the
+// rest. Since whole blocks hold a multiple of RPI rows, every lane leaves a
+// head's run at the same load, so the stepping from one run to the next is
+// uniform (scalar) and the loads need no per-lane index arithmetic beyond one
+// pointer add. A short last block takes a plain per-load (head, row) split.
 template <typename T, int D>
 __device__ __forceinline__ void wave_query_mean(const Geo& g, const T* __restrict__ q, int b, int kvh, int qb,
                                                 double* qbar, int lane) {
   constexpr int VEC = Wide<T>::kVec;
   constexpr int LPR = D / VEC;   // lanes covering one row
-  constexpr int RPI = 64 / LPR;  // rows per wave instruction
+  constexpr int RPI = 64 / LPR;  // rows per wave load
   constexpr int U = 16;          // loads in flight per lane
   const int col = (lane % LPR) * VEC;
   const int rsub = lane / LPR;
   const int r0 = qb * g.bs;
   const int rows = min(g.bs, g.N - r0);
   const int total = rows * g.G;  // (head, row) pairs
+  const T* base = q + (((int64_t)b * g.Hq + (int64_t)kvh * g.G) * g.N + r0) * D + col;
   double acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
-  for (int t = rsub; t < total; t += RPI * U) {
-    uint4 raw[U];
+  auto add = [&](const uint4& raw) {
+    float x[VEC];
+    Wide<T>::widen(raw, x);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // unconditional loads from a clamped (head, row) keep all of them in flight
-      const int tt = min(t + u * RPI, total - 1);
-      const int h = kvh * g.G + tt / rows;
-      raw[u] = Wide<T>::stream(q + (((int64_t)b * g.Hq + h) * g.N + r0 + tt % rows) * D + col);
+    for (int e = 0; e < VEC; ++e) acc[e] += (double)x[e];
+  };
+  if (rows % RPI == 0) {
+    const int groups = rows / RPI;      // wave loads per head's run
+    const int nsteps = groups * g.G;    // wave loads in all
+    const int64_t step = (int64_t)RPI * D;
+    const int64_t step_next = step + ((int64_t)g.N - rows) * D;  // last group of a run -> first of the next
+    const T* ptr = base + (int64_t)rsub * D;
+    int kr = 0;  // row group within the current run (uniform)
+    auto advance = [&]() {
+      const bool wrap = ++kr == groups;
+      kr = wrap ? 0 : kr;
+      ptr += wrap ? step_next : step;
+    };
+    int s = 0;
+    for (; s + U <= nsteps; s += U) {
+      uint4 raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        raw[u] = Wide<T>::stream(ptr);
+        advance();
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) add(raw[u]);
     }
+    if (s < nsteps) {
+      uint4 raw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float x[VEC];
-      Wide<T>::widen(raw[u], x);
+      for (int u = 0; u < U; ++u) {
+        const bool live = s + u < nsteps;  // uniform
+        raw[u] = Wide<T>::stream(live ? ptr : base);
+        if (live) advance();
+      }
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += t + u * RPI < total ? (double)x[e] : 0.0;
+      for (int u = 0; u < U; ++u)
+        if (s + u < nsteps) add(raw[u]);
+    }
+  } else {
+    for (int t = rsub; t < total; t += RPI * U) {
+      uint4 raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // unconditional loads from a clamped (head, row) keep all of them in flight
+        const int tt = min(t + u * RPI, total - 1);
+        raw[u] = Wide<T>::stream(base + ((int64_t)(tt / rows) * g.N + tt % rows) * D);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float x[VEC];
+        Wide<T>::widen(raw[u], x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += t + u * RPI < total ? (double)x[e] : 0.0;
+      }
     }
   }
 #pragma unroll
@@ -92,13 +142,18 @@ hipError_t launch_select_e(const Geo& g, const void* q, const float* pyr, int32_
 
 template <typename T, int D>
 hipError_t launch_select_t(const Geo& g, const void* q, const float* pyr, int32_t* idx, int32_t* cnt, hipStream_t s) {
-  switch (pool_slots_per_lane(g)) {
-    case 1: return launch_select_e<T, D, 1>(g, q, pyr, idx, cnt, s);
-    case 2: return launch_select_e<T, D, 2>(g, q, pyr, idx, cnt, s);
-    case 4: return launch_select_e<T, D, 4>(g, q, pyr, idx, cnt, s);
-    case 8: return launch_select_e<T, D, 8>(g, q, pyr, idx, cnt, s);
-    default: return launch_select_e<T, D, 16>(g, q, pyr, idx, cnt, s);
-  }
+  // the ranking's cost grows with the slots, so the pool gets the fewest that hold it
+  const int e = pool_slots_per_lane(g);
+  if (e <= 1) return launch_select_e<T, D, 1>(g, q, pyr, idx, cnt, s);
+  if (e <= 2) return launch_select_e<T, D, 2>(g, q, pyr, idx, cnt, s);
+  if (e <= 3) return launch_select_e<T, D, 3>(g, q, pyr, idx, cnt, s);
+  if (e <= 4) return launch_select_e<T, D, 4>(g, q, pyr, idx, cnt, s);
+  if (e <= 5) return launch_select_e<T, D, 5>(g, q, pyr, idx, cnt, s);
+  if (e <= 6) return launch_select_e<T, D, 6>(g, q, pyr, idx, cnt, s);
+  if (e <= 8) return launch_select_e<T, D, 8>(g, q, pyr, idx, cnt, s);
+  if (e <= 10) return launch_select_e<T, D, 10>(g, q, pyr, idx, cnt, s);
+  if (e <= 12) return launch_select_e<T, D, 12>(g, q, pyr, idx, cnt, s);
+  return launch_select_e<T, D, 16>(g, q, pyr, idx, cnt, s);
 }
 
 }  // namespace

@@ -20,20 +20,20 @@ namespace pisa {
 constexpr int kSelectThreads = 256;
 constexpr int kSelectWaves = kSelectThreads / 64;
 
-// Pool slots per lane (a power of two) covering the largest pool of any level:
+// Pool slots per lane, ceil(pool / 64), covering the largest pool of any level:
 // the top level's nodes, or K kept nodes' children plus the ancestor's.
 inline int pool_slots_per_lane(const Geo& g) {
   const int mmax = max(g.nodes[g.L - 1], g.K * g.f + g.f - 1);
-  int e = 1;
-  while (64 * e < mmax) e <<= 1;
-  return e;
+  return max(1, (mmax + 63) / 64);
 }
 
 // Per-wave LDS: scores staged from the scoring layout to the sort layout, the
-// nodes kept at the previous level, and the query mean.
+// level's pool as node ids, the nodes kept at the previous level, and the query
+// mean.
 template <int E, int D>
 struct WaveSmem {
   double sc[64 * E];
+  int node[64 * E];  // node held by each pool slot of the level, -1 if none
   int kept[kMaxTopK];
   int nkept;
   double qbar[D];
@@ -160,26 +160,24 @@ __device__ __forceinline__ int slot_node(int p, int nchild, int f, const int* ke
   return p < nchild ? kept[p / f] * f + p % f : anc_first + (p - nchild);
 }
 
-// Score pool slots [0, M) into sm.sc (fp64 dot products with the query mean).
-// 16 lanes per node, four nodes per wave instruction, four instructions in flight.
-template <int E, int D, int NWS>
-__device__ __forceinline__ void score_slots(const Geo& g, int l, int qb, const float* __restrict__ lvl, int M,
-                                            int nchild, int f, int anc_first, int lo, WaveSmem<E, D>& sm,
-                                            const double (&qv)[D / 16], int lane, int wave) {
+// Score pool slots [0, M) into sm.sc (fp64 dot products with the query mean);
+// the slots' nodes come from sm.node (-1: no node; its score is meaningless).
+// 16 lanes per node, four nodes per wave load, U loads in flight.
+template <int E, int D>
+__device__ __forceinline__ void score_slots(const float* __restrict__ lvl, int M, WaveSmem<E, D>& sm,
+                                            const double (&qv)[D / 16], int lane) {
   constexpr int DPL = D / 16;
   constexpr int U = 8;
-  const int grp = wave * 4 + (lane >> 4);  // 16-lane group among the NWS cooperating waves
+  const int grp = lane >> 4;
   const int sub = lane & 15;
-  for (int base = 0; base < M; base += 4 * NWS * U) {
+  for (int base = 0; base < M; base += 4 * U) {  // base + 4U <= 64E, so every slot read is in the table
     float4 x[U][DPL / 4];
-    bool use[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int p = base + u * 4 * NWS + grp;
-      const int n = p < M ? slot_node(p, nchild, f, sm.kept, anc_first) : 0;
-      use[u] = p < M && node_ok(g, l, n, qb, lo);
-      // unused slots read node 0 (always present) so that no load is conditional
-      const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)(use[u] ? n : 0) * D + sub * DPL);
+      // slots without a node read node 0 (always present) so that no load is
+      // conditional; their scores are never ranked
+      const int n = max(sm.node[base + u * 4 + grp], 0);
+      const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)n * D + sub * DPL);
 #pragma unroll
       for (int e4 = 0; e4 < DPL / 4; ++e4) x[u][e4] = row[e4];
     }
@@ -194,33 +192,21 @@ __device__ __forceinline__ void score_slots(const Geo& g, int l, int qb, const f
         acc += qv[e4 * 4 + 3] * (double)x[u][e4].w;
       }
       acc = row16_sum(acc);
-      const int p = base + u * 4 * NWS + grp;
-      if (sub == 0 && p < M) sm.sc[p] = use[u] ? acc : -__builtin_inf();
+      if (sub == 0) sm.sc[base + u * 4 + grp] = acc;
     }
   }
 }
 
 // Descent of one wave for query block (or decode token) qb of one slab.
 // ps: the slab's pyramid; sm.qbar: the fp64 query mean (written by this wave).
-// Writes out_idx[0, K) ascending, -1 padded, and *out_cnt.
-// With NWS > 1 the NWS waves of a workgroup score each level's pool together
-// (more loads in flight when the pyramid is not cached) and wave 0 sorts.
-template <int NWS>
-__device__ __forceinline__ void sync_scorers() {
-  if constexpr (NWS > 1) __syncthreads();
-  else __builtin_amdgcn_wave_barrier();
-}
-
-// Descent of one wave for query block (or decode token) qb of one slab.
-// ps: the slab's pyramid; sm.qbar: the fp64 query mean (written by this wave).
 // Writes out_idx[0, K) ascending, -1 padded, and *out_cnt. A level whose valid
 // pool holds at most K nodes keeps them all, so it is not scored.
-template <int E, int D, int NWS = 1>
+template <int E, int D>
 __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb, int32_t* __restrict__ out_idx,
-                             int32_t* __restrict__ out_cnt, WaveSmem<E, D>& sm, int lane, int wave = 0) {
+                             int32_t* __restrict__ out_cnt, WaveSmem<E, D>& sm, int lane) {
   constexpr int DPL = D / 16;
   if (g.K == 0) {
-    if (lane == 0 && wave == 0) *out_cnt = 0;
+    if (lane == 0) *out_cnt = 0;
     return;
   }
   double qv[DPL];
@@ -233,19 +219,6 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
   int M = g.causal ? max(0, qb / g.span[L - 1] - lo) : g.nodes[L - 1];
   int nchild = 0;                      // slots that are children of kept nodes
   int anc_first = g.causal ? lo : 0;   // first node of the contiguous tail of the pool
-  // next level's pool: children of the kept nodes, then (causal) the complete
-  // children of the ancestor; invalid nodes are masked by node_ok
-  auto next_pool = [&](int l, int nk) {
-    nchild = nk * g.f;
-    if (g.causal) {
-      anc_first = (qb / g.span[l]) * g.f;
-      M = nchild + (qb / g.span[l - 1] - anc_first);
-    } else {
-      anc_first = 0;
-      M = nchild;
-    }
-    lo = g.j0 / g.span[l - 1];
-  };
   for (int l = L - 1; l >= 0; --l) {
     // slot ids and validity need no scores
     int id[E];
@@ -259,24 +232,18 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
       nvalid += __popcll(__ballot(valid));
     }
     const int nk = min(g.K, nvalid);
-    const bool ranked = nvalid > g.K;  // uniform across the cooperating waves
-    if (ranked) {
-      score_slots<E, D, NWS>(g, l, qb, ps + (int64_t)g.off[l] * D, M, nchild, g.f, anc_first, lo, sm, qv, lane,
-                             wave);
-      sync_scorers<NWS>();
-    }
-    if (NWS > 1 && wave != 0) {  // helpers: wait for wave 0's kept list, then go on
-      if (l == 0) return;
-      sync_scorers<NWS>();
-      next_pool(l, nk);
-      continue;
-    }
-    if (ranked) {
+    if (nvalid > g.K) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) sm.node[e * 64 + lane] = id[e] != INT_MAX ? id[e] : -1;
+      __builtin_amdgcn_wave_barrier();
+      score_slots<E, D>(ps + (int64_t)g.off[l] * D, M, sm, qv, lane);
+      __builtin_amdgcn_wave_barrier();
+      // the slot ids come back from the table, so they need no registers while scoring
       uint64_t key[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const int p = e * 64 + lane;
-        key[e] = (p < M && id[e] != INT_MAX) ? score_key(sm.sc[p]) : 0ull;
+        id[e] = sm.node[e * 64 + lane];
+        key[e] = id[e] >= 0 ? score_key(sm.sc[e * 64 + lane]) : 0ull;
       }
       wave_keep_best<E>(key, id, nk, (M + 63) >> 6, sm.kept, lane);
     } else {
@@ -301,8 +268,17 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
       if (lane == 0) *out_cnt = nk;
       return;
     }
-    sync_scorers<NWS>();
-    next_pool(l, nk);
+    // next level's pool: children of the kept nodes, then (causal) the complete
+    // children of the ancestor; invalid nodes are masked by node_ok
+    nchild = nk * g.f;
+    if (g.causal) {
+      anc_first = (qb / g.span[l]) * g.f;
+      M = nchild + (qb / g.span[l - 1] - anc_first);
+    } else {
+      anc_first = 0;
+      M = nchild;
+    }
+    lo = g.j0 / g.span[l - 1];
   }
 }
 
