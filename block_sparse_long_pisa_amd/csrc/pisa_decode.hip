@@ -48,7 +48,7 @@ __device__ __forceinline__ int seq_len_of(const Geo& g, const int32_t* lens, int
   return valid ? len : 1;
 }
 
-template <typename T, int D>
+template <typename T, int D, int E>
 __global__ __launch_bounds__(kDecSelThreads) void decode_select_kernel(Geo g, const T* __restrict__ q,
                                                                        const float* __restrict__ pyr,
                                                                        const int32_t* __restrict__ lens, int len_all,
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kDecSelThreads) void decode_select_kernel(Geo g, co
     qbar[c] = s / (double)g.G;
   }
   __syncthreads();
-  block_descend<D, kDecSelThreads, 8>(g, pyr + (int64_t)slab * g.off[g.L] * D, qb, qbar,
+  block_descend<D, kDecSelThreads, 8, E>(g, pyr + (int64_t)slab * g.off[g.L] * D, qb, qbar,
                                       idx + (int64_t)slab * g.K, cnt + slab, smem);
 }
 
@@ -396,8 +396,22 @@ static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, c
   const int splits = decode_splits(g, len_all);
   DecodeWs ws = carve(g, wsb, splits);
   const int slabs = g.B * g.Hkv;
-  hipLaunchKernelGGL((decode_select_kernel<T, D>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, (const T*)q, pyr, lens,
-                     len_all, ws.idx, ws.cnt);
+  {
+    const int e = pool_slots_per_lane(g);
+    const T* qt = (const T*)q;
+    if (e <= 2)
+      hipLaunchKernelGGL((decode_select_kernel<T, D, 2>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+                         len_all, ws.idx, ws.cnt);
+    else if (e <= 4)
+      hipLaunchKernelGGL((decode_select_kernel<T, D, 4>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+                         len_all, ws.idx, ws.cnt);
+    else if (e <= 8)
+      hipLaunchKernelGGL((decode_select_kernel<T, D, 8>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+                         len_all, ws.idx, ws.cnt);
+    else
+      hipLaunchKernelGGL((decode_select_kernel<T, D, 16>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+                         len_all, ws.idx, ws.cnt);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid(splits, slabs);

@@ -48,7 +48,7 @@ struct Pool {
 };
 
 template <typename T, int D, bool MX>
-__global__ __launch_bounds__(kPoolThreads) void pool_leaf_kernel(Geo g, const T* __restrict__ k,
+__global__ __launch_bounds__(kPoolThreads) __attribute__((amdgpu_waves_per_eu(4))) void pool_leaf_kernel(Geo g, const T* __restrict__ k,
                                                                   float* __restrict__ pyr, int chunk_blocks) {
   using PO = Pool<MX>;
   constexpr int VEC = Wide<T>::kVec;
@@ -73,17 +73,39 @@ __global__ __launch_bounds__(kPoolThreads) void pool_leaf_kernel(Geo g, const T*
     typename PO::Acc acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = PO::init();
-    for (int r = r0 + rsub; r < r1; r += RPI * kUnroll) {
+    // rounds of kUnroll loads covering whole row groups run unmasked; one masked
+    // round (clamped rows) takes the rest
+    const int nfull = (r1 - r0) / (RPI * kUnroll);  // uniform
+    const T* ptr = kb + (int64_t)(r0 + rsub) * D + col;
+#pragma unroll 1
+    for (int it = 0; it < nfull; ++it, ptr += RPI * kUnroll * D) {
+      uint4 raw[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) raw[u] = Wide<T>::stream(ptr + u * RPI * D);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        float x[VEC];
+        Wide<T>::widen(raw[u], x);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = PO::add(acc[e], x[e]);
+      }
+    }
+    const int r = r0 + nfull * RPI * kUnroll + rsub;
+    if (r0 + nfull * RPI * kUnroll < r1) {
       uint4 raw[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)  // unconditional loads from clamped rows, all in flight
         raw[u] = Wide<T>::stream(kb + (int64_t)min(r + u * RPI, r1 - 1) * D + col);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
+        // a clamped row repeats the block's last row: harmless for the maximum;
+        // for the sum its bits are cleared (+0.0) before widening
+        if constexpr (!MX)
+          if (r + u * RPI >= r1) raw[u] = make_uint4(0u, 0u, 0u, 0u);
         float x[VEC];
         Wide<T>::widen(raw[u], x);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = PO::add_row(acc[e], x[e], r + u * RPI < r1);
+        for (int e = 0; e < VEC; ++e) acc[e] = PO::add(acc[e], x[e]);
       }
     }
     // fold the row slots that share these columns

@@ -124,8 +124,8 @@ __device__ __forceinline__ void wave_keep_best(const uint64_t (&key)[E], const i
 // fp64 value of the lane a DPP row control names (both halves moved as dwords).
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double x) {
-  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), CTRL, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), CTRL, 0xF, 0xF, false);
+  const int lo = __builtin_amdgcn_mov_dpp(__double2loint(x), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(__double2hiint(x), CTRL, 0xF, 0xF, false);
   return __hiloint2double(hi, lo);
 }
 
@@ -284,9 +284,9 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
 
 // ---------------------------------------------------------------------------
 // Descent by a whole workgroup of NT threads for one query (decode): each level's
-// pool is scored in one round of loads (U nodes per 16-lane group), and each
-// candidate's place in the best-first order is its count of candidates that
-// rank before it, so no sort is needed.
+// pool is scored in rounds of loads (U nodes per 16-lane group), and the first
+// wave keeps the best K with the same threshold search as the per-wave descent
+// (E pool slots per lane cover the largest pool).
 
 struct BlockSmem {
   double sc[kPoolMax + 8];
@@ -295,7 +295,7 @@ struct BlockSmem {
   int nvalid;
 };
 
-template <int D, int NT, int U>
+template <int D, int NT, int U, int E>
 __device__ void block_descend(const Geo& g, const float* __restrict__ ps, int qb, const double* qbar,
                               int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt, BlockSmem& sm) {
   constexpr int DPL = D / 16;
@@ -356,11 +356,6 @@ __device__ void block_descend(const Geo& g, const float* __restrict__ ps, int qb
         }
       }
     }
-    // sentinels up to a multiple of 8 never rank before a candidate
-    if (ranked && tid < 8 && M + tid < ((M + 7) & ~7)) {
-      sm.sc[M + tid] = -__builtin_inf();
-      sm.id[M + tid] = INT_MAX;
-    }
     __syncthreads();
     const int nk = min(g.K, nvalid);
     if (!ranked) {  // keep every valid slot in slot order (few: at most K)
@@ -372,19 +367,16 @@ __device__ void block_descend(const Geo& g, const float* __restrict__ ps, int qb
         }
         for (int t = 0; t < c; ++t) sm.kept[t] = sm.id[t];
       }
-    } else
-    for (int p = tid; p < M; p += NT) {
-      const int myid = sm.id[p];
-      const double mys = sm.sc[p];
-      int r = 0;
-      // branch-free: eight independent broadcast reads per step (padded with sentinels)
-      const double* sp = sm.sc;
-      const int* ip = sm.id;
-      for (int q0 = 0; q0 < M; q0 += 8, sp += 8, ip += 8) {
+    } else if (tid < 64) {  // the first wave ranks the scored pool (M <= 64 E)
+      uint64_t key[E];
+      int id[E];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) r += ranks_before_nb(sp[u], ip[u], mys, myid);
+      for (int e = 0; e < E; ++e) {
+        const int p = e * 64 + tid;
+        id[e] = p < M ? sm.id[p] : INT_MAX;
+        key[e] = id[e] != INT_MAX ? score_key(sm.sc[p]) : 0ull;
       }
-      if (myid != INT_MAX && r < nk) sm.kept[r] = myid;
+      wave_keep_best<E>(key, id, nk, (M + 63) >> 6, sm.kept, tid);
     }
     __syncthreads();
     if (l == 0) {
