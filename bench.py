@@ -29,19 +29,19 @@ BF16_PEAK = 2.5e15  # flop/s, dense bf16 matrix cores
 # HBM traffic per launch on these two workloads, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch). Each counter is scaled by what
 # it reads for a plain device copy of 1 GiB into 1 GiB: FETCH_SIZE reports
-# 524334.9 KiB for the copy's 1 GiB of reads, WRITE_SIZE 1048576 KiB for its
+# 524332.9 KiB for the copy's 1 GiB of reads, WRITE_SIZE 1048576 KiB for its
 # writes. A figure holds only for the kernel source it was taken on: the sources
 # are hashed at run time and a changed kernel reports null.
-COPY_SCALE = {"fetch": 1048576.0 / 524334.9, "write": 1048576.0 / 1048576.0}
+COPY_SCALE = {"fetch": 1048576.0 / 524332.9, "write": 1048576.0 / 1048576.0}
 MEASURED_TRAFFIC = {
     # step: (sources, sha256 prefix of their bytes in this order, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attention": (("pisa_attn.hip", "pisa_internal.h"), "3f68bdf1fb3a17ee", 5680215.2, 1048576.0),
-    "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "9cf176bad1868934",
-                131118.2 + 265.5 + 41.5, 4608.5 + 64.0 + 8.0),  # leaf + two coarse levels
-    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "c7c2421cf7f284f2",
-               552424.7, 1110.0),
-    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h"), "c90bfc6f962a28c9",
-               50355.5 + 551148.7 + 5393.0, 80.0 + 9504.0 + 512.0),  # select + split attention + merge
+    "attention": (("pisa_attn.hip", "pisa_attn_common.h", "pisa_internal.h"), "07dfa7b53f93cbc9", 5738162.2, 1048576.0),
+    "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "b5aebc7ead8b5d23",
+                131123.6 + 338.0, 4608.3 + 72.0),  # leaf and levels 1, then levels 2 and up
+    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "666fe10b557b43ea",
+               526708.2, 1056.1),
+    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h"), "e8610b5a11e7a5ba",
+               47947.3 + 546820.2 + 5385.5, 80.0 + 9504.0 + 512.0),  # select + split attention + merge
 }
 
 
