@@ -226,8 +226,8 @@ def cpu_baseline(p, q, k, v, seed_units=0):
         lv = [lvl[0, 0] for lvl in pyr[0]]
         sels[int(qb)] = oracle.descend(lv, qbar[0][0, 0, qb], int(qb), p.top_k, p.sink_len, bs, p.fanout)
     t_sel = (time.perf_counter() - t0) / len(sel_units) * nb * p.heads_kv + t_qbar
-    # stage 3: attention for a sample of units (all G heads, all rows)
-    att_units = sel_units[::2]
+    # stage 3: attention for the same sample of units (all G heads, all rows)
+    att_units = sel_units
     t0 = time.perf_counter()
     for qb in att_units:
         sel = sels[int(qb)]
@@ -352,6 +352,32 @@ def run_prefill(args, dev):
                           "frac": flops / t_att / BF16_PEAK, "attended_pairs": pairs, "traffic": measured_traffic("attention")},
         },
     }
+
+    if args.fused:
+        # the fused selection + attention (one launch) on the same pyramid, beside
+        # the two launches it replaces
+        pisa.build_pyramid(cp, k, pyr)
+        for _ in range(args.warmup):
+            pisa.select_attend(cp, q, k, v, pyr, idx, cnt, out)
+        torch.cuda.synchronize()
+        fe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.fused_steps)]
+        for e in fe:
+            e[0].record()
+            pisa.select_attend(cp, q, k, v, pyr, idx, cnt, out)
+            e[1].record()
+        torch.cuda.synchronize()
+        t_fu = float(np.mean([e[0].elapsed_time(e[1]) for e in fe])) * 1e-3
+        log(f"fused select+attend {t_fu * 1e3:.3f} ms, against select + attention {(t_sel + t_att) * 1e3:.3f} ms")
+        result["fused"] = {
+            "workload": "the same prefill: pisa_select_attend (query mean, descent and attention in one launch) "
+                        "on the built pyramid",
+            "ms": t_fu * 1e3,
+            "two_launch_ms": (t_sel + t_att) * 1e3,
+            "step_ms": (t_pool + t_fu) * 1e3,
+            "tokens_per_s": p.batch * p.seq_len / (t_pool + t_fu),
+            "TFLOP/s": flops / t_fu / 1e12,
+            "frac": flops / t_fu / BF16_PEAK,
+        }
 
     if args.variants:
         # the variants on the same inputs: bidirectional (mean summaries) and
@@ -563,6 +589,10 @@ def main(argv=None):
                     help="also time the bidirectional and max-pool variants on the prefill workload (default)")
     ap.add_argument("--no-variants", dest="variants", action="store_false")
     ap.add_argument("--variant-steps", type=int, default=5)
+    ap.add_argument("--fused", dest="fused", action="store_true", default=True,
+                    help="also time the fused selection + attention on the prefill workload (default)")
+    ap.add_argument("--no-fused", dest="fused", action="store_false")
+    ap.add_argument("--fused-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args(argv)

@@ -28,6 +28,7 @@ __all__ = [
     "build_pyramid",
     "select_topk",
     "sparse_attn_fwd",
+    "select_attend",
     "sparse_attn_bwd_workspace_size",
     "sparse_attn_bwd",
     "decode_workspace_size",
@@ -45,6 +46,7 @@ EXPORTED_SYMBOLS = [
     "pisa_build_pyramid",
     "pisa_select_topk",
     "pisa_sparse_attn_fwd",
+    "pisa_select_attend",
     "pisa_sparse_attn_bwd_workspace_size",
     "pisa_sparse_attn_bwd",
     "pisa_decode_workspace_size",
@@ -130,6 +132,7 @@ def load_library():
         "pisa_build_pyramid": [P, vp, vp, vp],
         "pisa_select_topk": [P, vp, vp, vp, vp, vp],
         "pisa_sparse_attn_fwd": [P, vp, vp, vp, vp, vp, vp, vp, vp],
+        "pisa_select_attend": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "pisa_decode_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
         "pisa_sparse_attn_bwd_workspace_size": [P, ctypes.POINTER(ctypes.c_size_t)],
         "pisa_sparse_attn_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
@@ -254,6 +257,39 @@ def sparse_attn_fwd(p: Problem, q, k, v, idx, cnt, out=None, lse=None, want_lse:
     _check(lib.pisa_sparse_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(idx) if p.top_k else None,
                                     _ptr(cnt), _ptr(out), _ptr(lse), _stream(q)), "pisa_sparse_attn_fwd")
     return out, lse
+
+
+def select_attend(p: Problem, q, k, v, pyramid, idx=None, cnt=None, out=None, lse=None, want_lse: bool = False,
+                  want_idx: bool = False):
+    """Selection and attention in one launch (bf16, causal). Returns (out, lse, idx, cnt); idx and cnt are
+    written only when given or requested."""
+    torch = _torch()
+    lib = load_library()
+    nb = p.n_blocks
+    dt = _tdtype(p)
+    _expect(q, (p.batch, p.heads_q, p.seq_len, p.head_dim), dt, "q")
+    _expect(k, (p.batch, p.heads_kv, p.seq_len, p.head_dim), dt, "k")
+    _expect(v, (p.batch, p.heads_kv, p.seq_len, p.head_dim), dt, "v")
+    _expect(pyramid, (p.batch, p.heads_kv, pyramid_layout(p)[-1], p.head_dim), torch.float32, "pyramid")
+    if want_idx and idx is None:
+        idx = torch.empty((p.batch, p.heads_kv, nb, p.top_k), dtype=torch.int32, device=q.device)
+    if want_idx and cnt is None:
+        cnt = torch.empty((p.batch, p.heads_kv, nb), dtype=torch.int32, device=q.device)
+    if idx is not None:
+        _expect(idx, (p.batch, p.heads_kv, nb, p.top_k), torch.int32, "idx")
+    if cnt is not None:
+        _expect(cnt, (p.batch, p.heads_kv, nb), torch.int32, "cnt")
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, tuple(q.shape), dt, "out")
+    if lse is None and want_lse:
+        lse = torch.empty((p.batch, p.heads_q, p.seq_len), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _expect(lse, (p.batch, p.heads_q, p.seq_len), torch.float32, "lse")
+    _check(lib.pisa_select_attend(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(pyramid),
+                                  _ptr(idx) if (idx is not None and p.top_k) else None, _ptr(cnt), _ptr(out),
+                                  _ptr(lse), _stream(q)), "pisa_select_attend")
+    return out, lse, idx, cnt
 
 
 def prefill(p: Problem, q, k, v, want_lse: bool = False):

@@ -18,7 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "lib", "libpisa.so")
-SOURCES = ["pisa_api.hip", "pisa_pool.hip", "pisa_select.hip", "pisa_attn.hip", "pisa_attn_bwd.hip", "pisa_decode.hip"]
+SOURCES = ["pisa_api.hip", "pisa_pool.hip", "pisa_select.hip", "pisa_attn.hip", "pisa_attn_bwd.hip", "pisa_decode.hip",
+           "pisa_fused.hip"]
 ARCH = "gfx950"
 
 

@@ -188,6 +188,23 @@ pisa_status pisa_sparse_attn_fwd(const pisa_problem* p, const void* q, const voi
   return e == hipSuccess ? ok() : hip_fail(e, "pisa_sparse_attn_fwd launch");
 }
 
+pisa_status pisa_select_attend(const pisa_problem* p, const void* q, const void* k, const void* v,
+                               const float* pyramid, int32_t* idx, int32_t* cnt, void* out, float* lse,
+                               hipStream_t stream) {
+  pisa::Geo g;
+  pisa_status s = make_geo(p, &g);
+  if (s != PISA_OK) return s;
+  if (empty(g)) return ok();
+  if (g.dtype != PISA_BF16) return fail(PISA_ERR_UNSUPPORTED, "the fused path is implemented for bf16 only");
+  if (!g.causal) return fail(PISA_ERR_UNSUPPORTED, "the fused path is implemented for causal attention only");
+  if (q == nullptr || k == nullptr || v == nullptr || pyramid == nullptr || out == nullptr)
+    return fail(PISA_ERR_NULL, "q, k, v, pyramid or out is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(pyramid) || !aligned16(out))
+    return fail(PISA_ERR_ALIGN, "q, k, v, pyramid and out must be 16-byte aligned");
+  hipError_t e = pisa::launch_select_attn(g, q, k, v, pyramid, idx, cnt, out, lse, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "pisa_select_attend launch");
+}
+
 pisa_status pisa_sparse_attn_bwd_workspace_size(const pisa_problem* p, size_t* bytes) {
   pisa::Geo g;
   pisa_status s = make_geo(p, &g);

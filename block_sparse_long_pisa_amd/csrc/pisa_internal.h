@@ -93,6 +93,10 @@ hipError_t launch_select(const Geo& g, const void* q, const float* pyr, int32_t*
 hipError_t launch_attn(const Geo& g, const void* q, const void* k, const void* v, const int32_t* idx,
                        const int32_t* cnt, void* out, float* lse, hipStream_t s);
 
+// selection and attention in one launch (bf16, causal): idx and cnt nullable
+hipError_t launch_select_attn(const Geo& g, const void* q, const void* k, const void* v, const float* pyr,
+                              int32_t* idx, int32_t* cnt, void* out, float* lse, hipStream_t s);
+
 // backward of the sparse attention (bf16): rowdot, dQ, key lists, dK/dV, reduce
 size_t attn_bwd_workspace_bytes(const Geo& g);
 hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const void* v, const int32_t* idx,

@@ -144,6 +144,22 @@ pisa_status pisa_select_topk(const pisa_problem* p, const void* q, const float* 
 pisa_status pisa_sparse_attn_fwd(const pisa_problem* p, const void* q, const void* k, const void* v, const int32_t* idx,
                                  const int32_t* cnt, void* out, float* lse, hipStream_t stream);
 
+/* Selection and attention fused in one launch (the PISA page, "Des noyaux
+ * Triton qui ne matérialisent rien": similarity, selection and aggregation in
+ * one pass). Computes what pisa_select_topk followed by pisa_sparse_attn_fwd
+ * computes, from the same arguments:
+ *   q, k, v: as for pisa_sparse_attn_fwd; pyramid: from pisa_build_pyramid;
+ *   idx, cnt: nullable outputs, the selection as pisa_select_topk writes it;
+ *   out, lse: as for pisa_sparse_attn_fwd (lse nullable).
+ * Each workgroup of the attention grid computes its query block's mean and
+ * descends the pyramid itself before attending, so no selection passes through
+ * HBM. Implemented for bf16 causal problems; other problems return
+ * PISA_ERR_UNSUPPORTED. The selection equals pisa_select_topk's bit for bit and,
+ * given it, out and lse equal pisa_sparse_attn_fwd's bit for bit. */
+pisa_status pisa_select_attend(const pisa_problem* p, const void* q, const void* k, const void* v,
+                               const float* pyramid, int32_t* idx, int32_t* cnt, void* out, float* lse,
+                               hipStream_t stream);
+
 /* Device workspace (bytes) that pisa_sparse_attn_bwd needs for this problem. */
 pisa_status pisa_sparse_attn_bwd_workspace_size(const pisa_problem* p, size_t* bytes);
 

@@ -186,6 +186,23 @@ def test_backward_validation(lib):
     assert bwd(prob=_p(batch=0)) == OK
 
 
+def test_fused_validation(lib):
+    p = _p(seq_len=4096)
+    fake = ctypes.c_void_p(4096)
+
+    def fused(prob=p, pyr=fake, out=fake, k=fake, idx=fake, cnt=fake):
+        return lib.pisa_select_attend(ctypes.byref(prob), fake, k, fake, pyr, idx, cnt, out, None, None)
+
+    assert fused(pyr=None) == ENULL
+    assert fused(out=None) == ENULL
+    assert fused(k=ctypes.c_void_p(4104)) == EALIGN
+    assert fused(pyr=ctypes.c_void_p(4100)) == EALIGN
+    assert fused(prob=_p(seq_len=4096, dtype=pisa.F32)) == EUNSUP
+    assert fused(prob=_p(seq_len=4096, causal=0)) == EUNSUP
+    assert fused(prob=_p(batch=0)) == OK
+    assert lib.pisa_select_attend(None, fake, fake, fake, fake, None, None, fake, None, None) == ENULL
+
+
 def test_status_strings(lib):
     for s in range(7):
         assert lib.pisa_status_string(s)
