@@ -122,6 +122,17 @@ pisa_status check_decode(const pisa::Geo& g, const void* q, const void* k_cache,
 
 }  // namespace
 
+namespace pisa {
+
+hipError_t device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  return hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+}
+
+}  // namespace pisa
+
 extern "C" {
 
 const char* pisa_status_string(pisa_status s) {

@@ -19,6 +19,8 @@
 // online softmax in registers, and accumulates O^T += V^T P^T on the same
 // matrix cores, reading V^T fragments with gfx950's transposing LDS reads.
 // fp32 path: plain VALU, one thread per query row.
+#include <algorithm>
+
 #include "pisa_attn_fwd.h"
 
 namespace pisa {
@@ -39,18 +41,22 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
   __shared__ __attribute__((aligned(16))) uint16_t V1[TilePitch<D, BS>::VSIZE];
   __shared__ int sel[kMaxTopK];
 
-  // heaviest units first; consecutive workgroups walk the (batch, kv head) slabs
-  // so that one slab's workgroups land on one XCD
+  // Persistent: workgroup i takes the (unit, part) items i, i + gridDim.x, ...
+  // Items are ordered heaviest units first, and consecutive items walk the
+  // (batch, kv head) slabs, so that one slab's items land on one XCD.
   const int slabs = g.B * g.Hkv;
-  const int wg = blockIdx.x;
-  const int slab = wg % slabs;
-  const int part = (wg / slabs) % parts;
-  const int qb = g.nb - 1 - wg / (slabs * parts);
-  const int64_t unit = (int64_t)slab * g.nb + qb;
-  const int nsel = min(max(cnt[unit], 0), g.K);
-  for (int t = threadIdx.x; t < nsel; t += NT) sel[t] = idx[unit * g.K + t];
-  __syncthreads();
-  attend_unit<D, BS, NW>(g, q, k, v, out, lse, slab, part, qb, sel, nsel, K0, V0, K1, V1);
+  const int64_t items = (int64_t)g.nb * slabs * parts;
+  for (int64_t wg = blockIdx.x; wg < items; wg += gridDim.x) {
+    const int slab = (int)(wg % slabs);
+    const int part = (int)((wg / slabs) % parts);
+    const int qb = g.nb - 1 - (int)(wg / ((int64_t)slabs * parts));
+    const int64_t unit = (int64_t)slab * g.nb + qb;
+    const int nsel = min(max(cnt[unit], 0), g.K);
+    for (int t = threadIdx.x; t < nsel; t += NT) sel[t] = idx[unit * g.K + t];
+    __syncthreads();
+    attend_unit<D, BS, NW>(g, q, k, v, out, lse, slab, part, qb, sel, nsel, K0, V0, K1, V1);
+    __syncthreads();  // every wave is done with sel and the stages before the next item
+  }
 }
 
 // fp32: one thread per query row, keys streamed through LDS 32 at a time.
@@ -127,11 +133,18 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(Geo g, const float* __res
   }
 }
 
+constexpr int kAttnWgPerCu = 8;  // persistent workgroups per compute unit
+
 template <int D, int BS, int NW>
 hipError_t launch_bf16(const Geo& g, const void* q, const void* k, const void* v, const int32_t* idx,
                        const int32_t* cnt, void* out, float* lse, hipStream_t s) {
   const int parts = g.G * BS / 32 / NW;
-  const int64_t grid = (int64_t)g.nb * g.B * g.Hkv * parts;
+  const int64_t items = (int64_t)g.nb * g.B * g.Hkv * parts;
+  // a few items per workgroup: fewer workgroup launches and a short tail
+  int cus = 0;
+  hipError_t e = device_cus(&cus);
+  if (e != hipSuccess) return e;
+  const int64_t grid = std::min<int64_t>(items, (int64_t)kAttnWgPerCu * cus);
   hipLaunchKernelGGL((attn_bf16_kernel<D, BS, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, g,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, (uint16_t*)out, lse, parts);
   return hipGetLastError();

@@ -85,6 +85,9 @@ struct Wide<float> {
   __device__ __forceinline__ static void load(const float* p, float* out) { widen(raw(p), out); }
 };
 
+// compute units of the current device (the runtime's cached attribute)
+hipError_t device_cus(int* cus);
+
 // ---------------------------------------------------------------------------
 // launchers (each lives beside its kernels)
 
