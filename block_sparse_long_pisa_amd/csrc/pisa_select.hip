@@ -30,7 +30,7 @@ __device__ __forceinline__ void wave_query_mean(const Geo& g, const T* __restric
   constexpr int VEC = Wide<T>::kVec;
   constexpr int LPR = D / VEC;   // lanes covering one row
   constexpr int RPI = 64 / LPR;  // rows per wave load
-  constexpr int U = 16;          // loads in flight per lane
+  constexpr int U = 8;           // loads in flight per lane (six waves per SIMD keep enough in flight)
   const int col = (lane % LPR) * VEC;
   const int rsub = lane / LPR;
   const int r0 = qb * g.bs;
@@ -112,7 +112,7 @@ __device__ __forceinline__ void wave_query_mean(const Geo& g, const T* __restric
 
 // One wave per (batch, kv head, query block); four query blocks of one slab per workgroup.
 template <typename T, int D, int E>
-__global__ __launch_bounds__(kSelectThreads) __attribute__((amdgpu_waves_per_eu(4))) void select_kernel(Geo g, const T* __restrict__ q,
+__global__ __launch_bounds__(kSelectThreads) __attribute__((amdgpu_waves_per_eu(E <= 5 ? 6 : 4))) void select_kernel(Geo g, const T* __restrict__ q,
                                                                 const float* __restrict__ pyr,
                                                                 int32_t* __restrict__ idx, int32_t* __restrict__ cnt) {
   __shared__ WaveSmem<E, D> smem[kSelectWaves];

@@ -35,19 +35,8 @@ struct WaveSmem {
   double sc[64 * E];
   int node[64 * E];  // node held by each pool slot of the level, -1 if none
   int kept[kMaxTopK];
-  int nkept;
   double qbar[D];
 };
-
-__device__ __forceinline__ bool ranks_before(double sa, int ia, double sb, int ib) {
-  return sa > sb || (sa == sb && ia < ib);
-}
-
-// The same order without short-circuit evaluation: both operands are always
-// evaluated, so loads feeding it are never made conditional.
-__device__ __forceinline__ int ranks_before_nb(double sa, int ia, double sb, int ib) {
-  return (int)(sa > sb) | ((int)(sa == sb) & (int)(ia < ib));
-}
 
 // Order-preserving map of an fp64 score to an unsigned key (larger score,
 // larger key); -0.0 counts as +0.0, as equal scores must tie.
@@ -167,7 +156,7 @@ template <int E, int D>
 __device__ __forceinline__ void score_slots(const float* __restrict__ lvl, int M, WaveSmem<E, D>& sm,
                                             const double (&qv)[D / 16], int lane) {
   constexpr int DPL = D / 16;
-  constexpr int U = 8;
+  constexpr int U = 4;  // few registers: more waves per SIMD hide the latency instead
   const int grp = lane >> 4;
   const int sub = lane & 15;
   for (int base = 0; base < M; base += 4 * U) {  // base + 4U <= 64E, so every slot read is in the table
@@ -289,8 +278,8 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
 // (E pool slots per lane cover the largest pool).
 
 struct BlockSmem {
-  double sc[kPoolMax + 8];
-  int id[kPoolMax + 8];
+  double sc[kPoolMax];
+  int id[kPoolMax];
   int kept[kMaxTopK];
   int nvalid;
 };
