@@ -98,6 +98,10 @@ __device__ __forceinline__ void decode_tile(const Geo& g, int qb, int pos, const
   } else if (t < nfull + np + nsel) {
     j = sel[t - nfull - np];
     nvalid = g.bs;
+    if (j < 0 || j >= qb) {  // not a block this token may select: attend nothing
+      j = qb;
+      nvalid = 0;
+    }
   } else {
     j = qb;
     nvalid = pos - qb * g.bs + 1;
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T
     float x[RPT][VEC];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)  // unconditional loads (clamped rows): all in flight
-      Wide<T>::widen(Wide<T>::stream(kb + ((int64_t)j * g.bs + min(rsub + i * RP, nvalid - 1)) * D + col), x[i]);
+      Wide<T>::widen(Wide<T>::stream(kb + ((int64_t)j * g.bs + min(rsub + i * RP, max(nvalid, 1) - 1)) * D + col), x[i]);
     float part[NV];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(kDecThreads) void decode_attn_kernel(Geo g, const T
     float x[RPT][VEC];
 #pragma unroll
     for (int i = 0; i < RPT; ++i)  // unconditional loads (clamped rows): all in flight
-      Wide<T>::widen(Wide<T>::stream(vb + ((int64_t)j * g.bs + min(rsub + i * RP, nvalid - 1)) * D + col), x[i]);
+      Wide<T>::widen(Wide<T>::stream(vb + ((int64_t)j * g.bs + min(rsub + i * RP, max(nvalid, 1) - 1)) * D + col), x[i]);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int r = rsub + i * RP;

@@ -46,9 +46,9 @@ __device__ __forceinline__ uint64_t score_key(double s) {
 }
 
 // Keep the nk best of the wave's pool slots -- score descending, node index
-// ascending -- without sorting. Only slots e < ne can be in use (ne uniform);
-// key[e] is 0 for an empty slot, so only valid slots (nk <= their count) are
-// ever kept. A threshold is found bit by bit, most significant first, with
+// ascending -- without sorting. key[e] is 0 for an empty slot, so only valid
+// slots (nk <= their count) are ever kept, and empty slots need no test of
+// their own (a guard per slot group costs more than the count it would skip). A threshold is found bit by bit, most significant first, with
 // wave-wide counts of the keys at or above it. As soon as exactly nk keys lie at
 // or above the prefix found so far, those are the nk best and the search stops
 // (with distinct scores near the boundary this takes about as many bits as
@@ -57,16 +57,15 @@ __device__ __forceinline__ uint64_t score_key(double s) {
 // lowest node indices fill the rest. Writes the kept node ids to kept[] in slot
 // order. Counts are scalar and branch-free within a step.
 template <int E>
-__device__ __forceinline__ void wave_keep_best(const uint64_t (&key)[E], const int (&id)[E], int nk, int ne,
-                                               int* kept, int lane) {
+__device__ __forceinline__ void wave_keep_best(const uint64_t (&key)[E], const int (&id)[E], int nk, int* kept,
+                                               int lane) {
   uint64_t T = 0;
   bool exact = false;  // exactly nk keys are >= T
   for (int b = 63; b >= 0; --b) {
     const uint64_t cand = T | (1ull << b);
     int c = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (e < ne) c += __popcll(__ballot(key[e] >= cand));
+    for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] >= cand));
     if (c >= nk) {
       T = cand;
       if (c == nk) {
@@ -79,11 +78,10 @@ __device__ __forceinline__ void wave_keep_best(const uint64_t (&key)[E], const i
   if (!exact) {
     int above = 0, at = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (e < ne) {
-        above += __popcll(__ballot(key[e] > T));
-        at += __popcll(__ballot(key[e] == T));
-      }
+    for (int e = 0; e < E; ++e) {
+      above += __popcll(__ballot(key[e] > T));
+      at += __popcll(__ballot(key[e] == T));
+    }
     const int need = nk - above;  // >= 1 slots at T to keep
     // when more slots tie at T than are needed, keep those with index <= I, the
     // need-th smallest index among them (indices of valid slots are distinct)
@@ -93,8 +91,7 @@ __device__ __forceinline__ void wave_keep_best(const uint64_t (&key)[E], const i
         const int mid = lo + (hi - lo) / 2;
         int c = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-          if (e < ne) c += __popcll(__ballot(key[e] == T && id[e] <= mid));
+        for (int e = 0; e < E; ++e) c += __popcll(__ballot(key[e] == T && id[e] <= mid));
         if (c >= need) hi = mid; else lo = mid + 1;
       }
       I = lo;
@@ -234,7 +231,7 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
         id[e] = sm.node[e * 64 + lane];
         key[e] = id[e] >= 0 ? score_key(sm.sc[e * 64 + lane]) : 0ull;
       }
-      wave_keep_best<E>(key, id, nk, (M + 63) >> 6, sm.kept, lane);
+      wave_keep_best<E>(key, id, nk, sm.kept, lane);
     } else {
       // keep every valid slot, compacted in slot order
       int base = 0;
@@ -279,9 +276,9 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
 
 struct BlockSmem {
   double sc[kPoolMax];
-  int id[kPoolMax];
+  int id[kPoolMax];  // node held by each pool slot of the level, INT_MAX if none
   int kept[kMaxTopK];
-  int nvalid;
+  int wcnt[16];      // valid slots counted by each wave
 };
 
 template <int D, int NT, int U, int E>
@@ -289,7 +286,11 @@ __device__ void block_descend(const Geo& g, const float* __restrict__ ps, int qb
                               int32_t* __restrict__ out_idx, int32_t* __restrict__ out_cnt, BlockSmem& sm) {
   constexpr int DPL = D / 16;
   constexpr int NG = NT / 16;  // 16-lane groups
+  constexpr int NWV = NT / 64;
+  static_assert(NWV <= 16, "per-wave counts");
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int grp = tid >> 4;
   const int sub = tid & 15;
   if (g.K == 0) {
@@ -305,67 +306,72 @@ __device__ void block_descend(const Geo& g, const float* __restrict__ ps, int qb
   int nchild = 0, anc_first = lo;
   for (int l = L - 1; l >= 0; --l) {
     const float* lvl = ps + (int64_t)g.off[l] * D;
-    // valid slots need no scores; a level with at most K of them keeps them all
+    // the level's pool as node ids (INT_MAX: no candidate), and its valid count
     int nv_local = 0;
-    for (int p = tid; p < M; p += NT) nv_local += slot_node(p, nchild, g.f, sm.kept, anc_first) >= lo ? 1 : 0;
-    if (tid == 0) sm.nvalid = 0;
+    for (int p0 = 0; p0 < M; p0 += NT) {
+      const int p = p0 + tid;
+      const int n = p < M ? slot_node(p, nchild, g.f, sm.kept, anc_first) : INT_MAX;
+      const bool valid = p < M && n >= lo;
+      if (p < M) sm.id[p] = valid ? n : INT_MAX;
+      nv_local += __popcll(__ballot(valid));
+    }
+    if (lane == 0) sm.wcnt[wave] = nv_local;
     __syncthreads();
-    if (nv_local) atomicAdd(&sm.nvalid, nv_local);
-    __syncthreads();
-    const int nvalid = sm.nvalid;
-    const bool ranked = nvalid > g.K;
-    for (int base = 0; ranked && base < M; base += NG * U) {
-      float4 x[U][DPL / 4];
-      int node[U];
-      bool use[U];
+    int nvalid = 0;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int p = base + u * NG + grp;
-        node[u] = p < M ? slot_node(p, nchild, g.f, sm.kept, anc_first) : 0;
-        use[u] = p < M && node[u] >= lo;
-        const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)(use[u] ? node[u] : 0) * D + sub * DPL);
+    for (int w = 0; w < NWV; ++w) nvalid += sm.wcnt[w];
+    const int nk = min(g.K, nvalid);
+    if (nvalid > g.K) {  // score the pool; a level with at most K valid slots keeps them all
+      for (int base = 0; base < M; base += NG * U) {
+        float4 x[U][DPL / 4];
 #pragma unroll
-        for (int e4 = 0; e4 < DPL / 4; ++e4) x[u][e4] = row[e4];
-      }
+        for (int u = 0; u < U; ++u) {
+          const int p = base + u * NG + grp;
+          const int n = p < M ? sm.id[p] : INT_MAX;
+          // slots without a node read node 0 (always present) so that no load is conditional
+          const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)(n != INT_MAX ? n : 0) * D + sub * DPL);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        double acc = 0.0;
-#pragma unroll
-        for (int e4 = 0; e4 < DPL / 4; ++e4) {
-          acc += qv[e4 * 4 + 0] * (double)x[u][e4].x;
-          acc += qv[e4 * 4 + 1] * (double)x[u][e4].y;
-          acc += qv[e4 * 4 + 2] * (double)x[u][e4].z;
-          acc += qv[e4 * 4 + 3] * (double)x[u][e4].w;
+          for (int e4 = 0; e4 < DPL / 4; ++e4) x[u][e4] = row[e4];
         }
-        acc = row16_sum(acc);
-        const int p = base + u * NG + grp;
-        if (sub == 0 && p < M) {
-          sm.sc[p] = use[u] ? acc : -__builtin_inf();
-          sm.id[p] = use[u] ? node[u] : INT_MAX;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          double acc = 0.0;
+#pragma unroll
+          for (int e4 = 0; e4 < DPL / 4; ++e4) {
+            acc += qv[e4 * 4 + 0] * (double)x[u][e4].x;
+            acc += qv[e4 * 4 + 1] * (double)x[u][e4].y;
+            acc += qv[e4 * 4 + 2] * (double)x[u][e4].z;
+            acc += qv[e4 * 4 + 3] * (double)x[u][e4].w;
+          }
+          acc = row16_sum(acc);
+          const int p = base + u * NG + grp;
+          if (sub == 0 && p < M) sm.sc[p] = acc;
         }
       }
     }
     __syncthreads();
-    const int nk = min(g.K, nvalid);
-    if (!ranked) {  // keep every valid slot in slot order (few: at most K)
-      if (tid == 0) {
-        int c = 0;
-        for (int p = 0; p < M; ++p) {
-          const int n = slot_node(p, nchild, g.f, sm.kept, anc_first);
-          if (n >= lo) sm.id[c++] = n;
-        }
-        for (int t = 0; t < c; ++t) sm.kept[t] = sm.id[t];
-      }
-    } else if (tid < 64) {  // the first wave ranks the scored pool (M <= 64 E)
-      uint64_t key[E];
+    if (tid < 64) {  // the first wave keeps the level's best (M <= 64 E)
       int id[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int p = e * 64 + tid;
         id[e] = p < M ? sm.id[p] : INT_MAX;
-        key[e] = id[e] != INT_MAX ? score_key(sm.sc[p]) : 0ull;
       }
-      wave_keep_best<E>(key, id, nk, (M + 63) >> 6, sm.kept, tid);
+      if (nvalid > g.K) {
+        uint64_t key[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) key[e] = id[e] != INT_MAX ? score_key(sm.sc[e * 64 + tid]) : 0ull;
+        wave_keep_best<E>(key, id, nk, sm.kept, tid);
+      } else {
+        // every valid slot, compacted in slot order
+        int base = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const unsigned long long m = __ballot(id[e] != INT_MAX);
+          if (id[e] != INT_MAX) sm.kept[base + __popcll(m & ((1ull << tid) - 1))] = id[e];
+          base += __popcll(m);
+        }
+      }
     }
     __syncthreads();
     if (l == 0) {
