@@ -36,8 +36,9 @@ struct DecodeWs {
 };
 
 // One workgroup of 512 threads per (batch, kv head): mean of the group's query
-// rows, then the descent with each level's pool scored in few rounds of loads
-// (the decode pyramid comes from HBM) and ranked by counting.
+// rows, then the workgroup descent, with each level's pool scored in few rounds
+// of loads (the decode pyramid comes from HBM) and the best K kept by the first
+// wave's threshold search.
 constexpr int kDecSelThreads = 512;
 
 // Cache length of sequence b: from the per-sequence array when there is one.
