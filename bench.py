@@ -187,6 +187,46 @@ def append_bytes(p, old_lens, new_lens):
 
 
 # ---------------------------------------------------------------------------
+# what this GPU reaches on plain library work (context for the peaks)
+
+
+def achievable_probes(torch, dev, reps=10):
+    """A large device copy (torch copy_, 2 GiB into 2 GiB; read + write bytes) and
+    a dense bf16 GEMM (torch matmul, 8192^3). Reported beside the published peaks,
+    which stay the denominators of every fraction."""
+    x = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    a = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    bm = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    for _ in range(3):
+        y.copy_(x)
+        torch.matmul(a, bm)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    for _ in range(reps):
+        y.copy_(x)
+    e[1].record()
+    for _ in range(reps):
+        torch.matmul(a, bm)
+    e[2].record()
+    torch.cuda.synchronize()
+    t_read = e[0].elapsed_time(e[1]) * 1e-3 / reps
+    t_gemm = e[1].elapsed_time(e[2]) * 1e-3 / reps
+    copy_bw = 2 * x.numel() * 4 / t_read
+    gemm = 2.0 * 8192 ** 3 / t_gemm
+    del x, y, a, bm
+    torch.cuda.empty_cache()
+    log(f"probes: device copy {copy_bw / 1e9:.0f} GB/s (read + write), bf16 GEMM {gemm / 1e12:.0f} TFLOP/s")
+    return {
+        "copy_GB/s": copy_bw / 1e9, "copy_frac": copy_bw / HBM_PEAK,
+        "bf16_gemm_TFLOP/s": gemm / 1e12, "bf16_gemm_frac": gemm / BF16_PEAK,
+        "what": "torch copy_ of 2 GiB into 2 GiB (bytes read + written); torch matmul of two 8192x8192 bf16 "
+                "matrices",
+    }
+
+
+# ---------------------------------------------------------------------------
 # CPU oracle on a bounded sample
 
 
@@ -454,6 +494,9 @@ def run_prefill(args, dev):
         }
         del dout, dq, dk, dv, bws, lse
 
+    if args.probes:
+        result["achievable"] = achievable_probes(torch, dev)
+
     if args.copy_calibration:
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev)
         bcopy = torch.empty_like(a)
@@ -593,6 +636,9 @@ def main(argv=None):
                     help="also time the fused selection + attention on the prefill workload (default)")
     ap.add_argument("--no-fused", dest="fused", action="store_false")
     ap.add_argument("--fused-steps", type=int, default=5)
+    ap.add_argument("--probes", dest="probes", action="store_true", default=True,
+                    help="also measure a plain stream read and a dense bf16 GEMM on this GPU (default)")
+    ap.add_argument("--no-probes", dest="probes", action="store_false")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args(argv)
