@@ -59,6 +59,7 @@ __all__ = [
     "query_block_means",
     "descend",
     "select",
+    "selection_report",
     "attended_keys",
     "attend",
     "attend_block",
@@ -194,6 +195,32 @@ def descend(levels: Sequence[np.ndarray], qbar: np.ndarray, qb: int, top_k: int,
         nxt += list(range(anc[l] * fanout, anc[l - 1]))  # complete children of the ancestor
         pool = sorted(c for c in nxt if useful(c, l - 1))
     raise AssertionError("unreachable")
+
+
+def selection_report(trace: list, top_k: int, fanout: int, targets: Sequence[int] = ()) -> dict:
+    """Self-report of one descent, from its `trace` (see `descend`).
+
+    gaps: for every level whose pool held more than `top_k` nodes, the margin
+      between the K-th and (K+1)-th best scores, i.e. how far the keep/prune
+      boundary was from a tie (0.0 for a tie broken by index);
+    pruned: for every target block, the level at which its ancestor was scored
+      and not kept, or None when that never happened (the block was selected, or
+      never scored).
+    """
+    gaps = {}
+    for t in trace:
+        if len(t["pool"]) > top_k:
+            order = sorted(range(len(t["pool"])), key=lambda i: (-t["scores"][i], t["pool"][i]))
+            gaps[t["level"]] = float(t["scores"][order[top_k - 1]] - t["scores"][order[top_k]])
+    pruned = {}
+    for j in targets:
+        pruned[j] = None
+        for t in trace:
+            a = j // fanout ** t["level"]
+            if a in t["pool"] and a not in t["kept"]:
+                pruned[j] = t["level"]
+                break
+    return dict(gaps=gaps, pruned=pruned)
 
 
 def select(pyramid: Sequence[np.ndarray], qbar: np.ndarray, top_k: int, sink_len: int, block_size: int,

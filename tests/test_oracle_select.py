@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import gen
-from oracle import build_pyramid, descend, query_block_means, select
+from oracle import build_pyramid, descend, query_block_means, select, selection_report
 
 
 def _blocks_keys(means, bs):
@@ -46,6 +46,41 @@ def test_hand_worked_pruning_differs_from_brute_force():
     lv = [p[0, 0] for p in build_pyramid(k, 2, 2, 3)]
     assert descend(lv, np.array([1.0]), 7, 2, 0, 2, 2) == [0, 3]
     assert _brute_force(lv[0], np.array([1.0]), 7, 2, 0) == [3, 4]
+
+
+def test_selection_report_on_the_hand_worked_pruning():
+    # level 1 scores the nodes (5, 1) -> 3, (2, 9) -> 5.5, (8, -10) -> -1 and keeps two:
+    # boundary margin 3 - (-1) = 4; level 0 scores blocks {0, 1, 2, 3, 6} = 5, 1, 2, 9, 0:
+    # margin 5 - 2 = 3. Block 4's node is dropped at level 1; block 3 is selected.
+    k = _blocks_keys([5, 1, 2, 9, 8, -10, 0, 7], 2)
+    lv = [p[0, 0] for p in build_pyramid(k, 2, 2, 3)]
+    tr = []
+    assert descend(lv, np.array([1.0]), 7, 2, 0, 2, 2, tr) == [0, 3]
+    rep = selection_report(tr, 2, 2, targets=[4, 3, 5])
+    assert rep["gaps"] == {1: 4.0, 0: 3.0}
+    assert rep["pruned"] == {4: 1, 3: None, 5: 1}
+
+
+def test_selection_report_names_the_level_that_drops_a_planted_block():
+    # deep random trees: a block the brute force ranks first but the descent
+    # misses is reported pruned at some level >= 1; a selected block never is
+    N, d, bs, f, L, K = 4096, 8, 16, 4, 4, 2
+    q, k, pyr, qbar = _random_case(7, N, d, bs, f, L)
+    lv = [p[0, 0] for p in pyr]
+    seen = 0
+    for qb in range(1, 256):
+        tr = []
+        sel = descend(lv, qbar[0, 0, qb], qb, K, 0, bs, f, tr)
+        bf = _brute_force(lv[0], qbar[0, 0, qb], qb, K, 0)
+        rep = selection_report(tr, K, f, targets=bf)
+        for j in bf:
+            if j in sel:
+                assert rep["pruned"][j] is None
+            else:
+                assert rep["pruned"][j] is not None and rep["pruned"][j] >= 1
+                seen += 1
+        assert all(g >= 0.0 for g in rep["gaps"].values())
+    assert seen > 0
 
 
 def _random_case(seed, N, d, bs, f, L, Hq=1, Hkv=1):
