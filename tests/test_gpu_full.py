@@ -60,9 +60,22 @@ def test_full_prefill(cfg_id):
     assert_pyramid_equal(g_levels, o_levels)
     log("  pyramid bit-exact; oracle selection of every query block")
     qbar = oracle.query_block_means(qh, p.heads_kv, p.block_size)
-    oi, oc = oracle.select(o_levels, qbar, p.top_k, p.sink_len, p.block_size, p.fanout)
+    traces = {}
+    oi, oc = oracle.select(o_levels, qbar, p.top_k, p.sink_len, p.block_size, p.fanout, traces=traces)
     assert_selection_equal(gi, gc, oi, oc)
-    log(f"  {oc.size} selections bit-exact; oracle attention on sampled blocks")
+    # how close the keep/prune boundaries came to a tie, against the scores' size:
+    # exact equality is meaningful because the smallest margin is far above the
+    # rounding of an fp64 dot product of d terms (~d * 2^-53 relative)
+    rel = [g / max(abs(t["scores"]).max(), 1e-300) for tr in traces.values()
+           for t in tr if len(t["pool"]) > p.top_k
+           for g in [oracle.selection_report([t], p.top_k, p.fanout)["gaps"][t["level"]]]]
+    if rel:
+        assert min(rel) > 1e3 * p.head_dim * 2.0 ** -53, f"a boundary within rounding of a tie: {min(rel):.2e}"
+    dropped = sum(1 for n in man["needles"] if n["survived"] and oracle.selection_report(
+        traces[(n["b"], n["g"], n["qb"])], p.top_k, p.fanout, [n["target"]])["pruned"][n["target"]] is not None)
+    log(f"  {oc.size} selections bit-exact; smallest relative boundary margin "
+        f"{min(rel) if rel else float('nan'):.2e}; planted blocks dropped by coarse levels: {dropped}; "
+        "oracle attention on sampled blocks")
     units = _sample_units(p, man) if cfg_id != 1 else None
     o, ol = oracle.attend(qh, kh, vh, oi, oc, p.sink_len, p.block_size, p.scale, blocks=units)
     err = assert_outputs_close(p, to_host(out), o, to_host(lse), ol)
