@@ -35,13 +35,14 @@ BF16_PEAK = 2.5e15  # flop/s, dense bf16 matrix cores
 COPY_SCALE = {"fetch": 1048576.0 / 524332.9, "write": 1048576.0 / 1048576.0}
 MEASURED_TRAFFIC = {
     # step: (sources, sha256 prefix of their bytes in this order, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attention": (("pisa_attn.hip", "pisa_attn_common.h", "pisa_internal.h"), "07dfa7b53f93cbc9", 5738162.2, 1048576.0),
-    "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "b5aebc7ead8b5d23",
-                131123.6 + 338.0, 4608.3 + 72.0),  # leaf and levels 1, then levels 2 and up
-    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "666fe10b557b43ea",
-               526708.2, 1056.1),
-    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h"), "e8610b5a11e7a5ba",
-               47947.3 + 546820.2 + 5385.5, 80.0 + 9504.0 + 512.0),  # select + split attention + merge
+    "attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "5d3f16d4682ba197",
+                  5781483.0, 1048578.5),
+    "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "b7af1c49483bc6e8",
+                131123.5 + 338.0, 4608.1 + 72.0),  # leaf and levels 1, then levels 2 and up
+    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "5ab994057d218ca3",
+               526688.2, 1056.1),
+    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h"), "f1827f980778f08a",
+               47923.1 + 546819.3 + 5393.0, 80.0 + 9504.0 + 512.0),  # select + split attention + merge
 }
 
 
