@@ -31,11 +31,13 @@ constexpr int kListThreads = 256;
 enum : int { kFull = 0, kSinkPart = 1, kLocal = 2 };
 
 // ---------------------------------------------------------------------------
-// D_i = dO_i . O_i, 16 lanes per row
+// D_i = dO_i . O_i, 16 lanes per row; beside it lse_i in log2 units, so that the
+// key-centric pass takes p = exp2(s c - lse2) with one fused multiply-add
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restrict__ dout,
-                                                         const uint16_t* __restrict__ out, float* __restrict__ rowdot,
+                                                         const uint16_t* __restrict__ out, const float* __restrict__ lse,
+                                                         float* __restrict__ rowdot, float* __restrict__ lse2,
                                                          int64_t rows) {
   constexpr int PER = D / 16;  // bf16 per lane
   const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -55,7 +57,10 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restr
   }
 #pragma unroll
   for (int sh = 1; sh < 16; sh <<= 1) s += __shfl_xor(s, sh);
-  if (sub == 0 && r < rows) rowdot[r] = s;
+  if (sub == 0 && r < rows) {
+    rowdot[r] = s;
+    lse2[r] = lse[r] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -339,65 +344,92 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(const int32_t* __restric
 template <int D, int BS>
 __device__ __forceinline__ void kv_tile(const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
                                         f32x16_t (&dk)[D / 32], f32x16_t (&dv)[D / 32], const uint16_t* qs,
-                                        const uint16_t* os, const float* ls, const float* rs, int rows, int kind,
-                                        int key, int keylim, int l32, int hi, int offq, int offo, float c) {
+                                        const uint16_t* os, const float* ls, const float* rs, bool mask, int rows,
+                                        int rlo, int l32, int hi, int offq, int offo, float c) {
   constexpr int NDS = D / 16, NDB = D / 32;
   constexpr int QC = 32;  // query rows per chunk (one 32-row block keeps the registers in bounds)
-  constexpr int NQB = QC / 32;
   constexpr int PK = TilePitch<D, BS>::K, PV = TilePitch<D, BS>::V;
-  const bool causal = kind == kLocal;
 #pragma unroll
   for (int ch = 0; ch < BS / QC; ++ch) {
     if (ch > 0 && ch * QC >= rows) break;
-    f32x16_t s[NQB], dp[NQB];
+    f32x16_t s, dp;
 #pragma unroll
-    for (int qk = 0; qk < NQB; ++qk) {
+    for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+    // every LDS fragment of the chunk is requested before its first product: with
+    // one wave per SIMD nothing else hides the LDS latency
+    bf16x8_t fq[NDS], fo[NDS], tv[2][NDB], tq[2][NDB];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[qk][i] = dp[qk][i] = 0.f;
+    for (int ds = 0; ds < NDS; ++ds) {
+      const int row = ch * QC + l32, col = ds * 16 + hi * 8;
+      fq[ds] = row_frag<PK>(qs, row, col);
+      fo[ds] = row_frag<PV>(os, row, col);
+    }
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const int row = ch * QC + qk * 32 + l32, col = ds * 16 + hi * 8;
-        s[qk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<PK>(qs, row, col), kf[ds], s[qk], 0, 0, 0);
-        dp[qk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<PV>(os, row, col), vf[ds], dp[qk], 0, 0, 0);
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        tv[hh][db] = tr_frag<PV>(os, offo, ch * QC + hh * 16, db);
+        tq[hh][db] = tr_frag<PK>(qs, offq, ch * QC + hh * 16, db);
+      }
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[ds], kf[ds], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo[ds], vf[ds], dp, 0, 0, 0);
+    }
+    // element i is query row r = ch*QC + (i/4)*8 + hi*4 + i%4; ls holds lse in
+    // log2 units
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const float4 l4 = *reinterpret_cast<const float4*>(ls + ch * QC + i4 * 8 + hi * 4);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[i4 * 4 + e] = fast_exp2(fmaf(s[i4 * 4 + e], c, -lv[e]));
+    }
+    if (mask) {  // uniform: only partial-sink, causal and ragged tiles; rows [rlo, rows) count for this key
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = ch * QC + (i >> 2) * 8 + hi * 4 + (i & 3);
+        s[i] = r >= rlo && r < rows ? s[i] : 0.f;
       }
     }
-    // element i of block qk is query row r = ch*QC + qk*32 + (i/4)*8 + hi*4 + i%4
 #pragma unroll
-    for (int qk = 0; qk < NQB; ++qk)
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const float4 d4 = *reinterpret_cast<const float4*>(rs + ch * QC + i4 * 8 + hi * 4);
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int r0 = ch * QC + qk * 32 + i4 * 8 + hi * 4;
-        const float4 l4 = *reinterpret_cast<const float4*>(ls + r0);
-        const float4 d4 = *reinterpret_cast<const float4*>(rs + r0);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      for (int e = 0; e < 4; ++e) dp[i4 * 4 + e] = s[i4 * 4 + e] * (dp[i4 * 4 + e] - dv4[e]);
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i4 * 4 + e;
-          const int r = r0 + e;
-          const bool on = r < rows && key < keylim && (!causal || (key & (BS - 1)) <= r);
-          const float p = on ? fast_exp2(fmaf(s[qk][i], c, -lv[e] * kLog2e)) : 0.f;
-          s[qk][i] = p;
-          dp[qk][i] = p * (dp[qk][i] - dv4[e]);
-        }
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x8_t pb, sb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[e] = (__bf16)s[hh * 8 + e];
+        sb[e] = (__bf16)dp[hh * 8 + e];
       }
 #pragma unroll
-    for (int qk = 0; qk < NQB; ++qk)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8_t pb, sb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[e] = (__bf16)s[qk][hh * 8 + e];
-          sb[e] = (__bf16)dp[qk][hh * 8 + e];
-        }
-        const int r = ch * QC + qk * 32 + hh * 16;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<PV>(os, offo, r, db), pb, dv[db], 0, 0, 0);
-          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<PK>(qs, offq, r, db), sb, dk[db], 0, 0, 0);
-        }
+      for (int db = 0; db < NDB; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tv[hh][db], pb, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[hh][db], sb, dk[db], 0, 0, 0);
       }
+    }
   }
+}
+
+// One (query block, head) stage. Whole tiles of full kind (every row and key
+// counts) skip the mask; otherwise the rows that count for this lane's key are
+// [rlo, rows): rlo = the key's own row on the causal diagonal, past the block
+// for a key outside the sink (partial sink tile) or the sequence.
+template <int D, int BS>
+__device__ __forceinline__ void kv_stage(const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
+                                         f32x16_t (&dk)[D / 32], f32x16_t (&dv)[D / 32], const uint16_t* qs,
+                                         const uint16_t* os, const float* ls, const float* rs, const Geo& g, int qb,
+                                         int kind, int j, int key, int l32, int hi, int offq, int offo, float c) {
+  const int rows = min(BS, g.N - qb * BS);
+  const bool mask = !(kind == kFull && rows == BS && (j + 1) * BS <= g.N);
+  const bool key_ok = key < (kind == kSinkPart ? g.sink : g.N);
+  const int rlo = !key_ok ? BS : kind == kLocal ? (key & (BS - 1)) : 0;
+  kv_tile<D, BS>(kf, vf, dk, dv, qs, os, ls, rs, mask, rows, rlo, l32, hi, offq, offo, c);
 }
 
 // Issue the copies of one (query block, head) stage: Q and dO rows, and the
@@ -426,7 +458,7 @@ __global__ __launch_bounds__(BS / 32 * 64) void bwd_kv_kernel(Geo g, const uint1
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
                                                               const uint16_t* __restrict__ dout,
-                                                              const float* __restrict__ lse,
+                                                              const float* __restrict__ lse2,
                                                               const float* __restrict__ rowdot,
                                                               const int32_t* __restrict__ lists,
                                                               const int32_t* __restrict__ list_off,
@@ -487,30 +519,24 @@ __global__ __launch_bounds__(BS / 32 * 64) void bwd_kv_kernel(Geo g, const uint1
     kind = e >> 28;
     h = kvh * g.G + t % g.G;
   };
-  // keys of the block that count for a tile kind: the sink's for a partial sink
-  // tile, else those inside the sequence
-  auto keylim = [&](int kind) { return kind == kSinkPart ? g.sink : g.N; };
-
   int qb, h, kind;
   entry(0, qb, h, kind);
-  issue_rows<D, BS, NW>(g, q, dout, lse, rowdot, b, h, qb, Q0, O0, L0, R0, wave, lane, plan);
+  issue_rows<D, BS, NW>(g, q, dout, lse2, rowdot, b, h, qb, Q0, O0, L0, R0, wave, lane, plan);
   for (int t = 0; t < npairs; t += 2) {
     wait_loads_and_sync();
     int qb1 = 0, h1 = 0, kind1 = 0;
     if (t + 1 < npairs) {
       entry(t + 1, qb1, h1, kind1);
-      issue_rows<D, BS, NW>(g, q, dout, lse, rowdot, b, h1, qb1, Q1, O1, L1, R1, wave, lane, plan);
+      issue_rows<D, BS, NW>(g, q, dout, lse2, rowdot, b, h1, qb1, Q1, O1, L1, R1, wave, lane, plan);
     }
-    kv_tile<D, BS>(kf, vf, dk, dv, Q0, O0, L0, R0, min(BS, g.N - qb * BS), kind, key, keylim(kind), l32, hi, offq,
-                   offo, c);
+    kv_stage<D, BS>(kf, vf, dk, dv, Q0, O0, L0, R0, g, qb, kind, j, key, l32, hi, offq, offo, c);
     if (t + 1 >= npairs) break;
     wait_loads_and_sync();
     if (t + 2 < npairs) {
       entry(t + 2, qb, h, kind);
-      issue_rows<D, BS, NW>(g, q, dout, lse, rowdot, b, h, qb, Q0, O0, L0, R0, wave, lane, plan);
+      issue_rows<D, BS, NW>(g, q, dout, lse2, rowdot, b, h, qb, Q0, O0, L0, R0, wave, lane, plan);
     }
-    kv_tile<D, BS>(kf, vf, dk, dv, Q1, O1, L1, R1, min(BS, g.N - qb1 * BS), kind1, key, keylim(kind1), l32, hi, offq,
-                   offo, c);
+    kv_stage<D, BS>(kf, vf, dk, dv, Q1, O1, L1, R1, g, qb1, kind1, j, key, l32, hi, offq, offo, c);
   }
   // partial sums of this segment: [segment][key of the block][d], fp32
   float* pk = pdk + ((int64_t)w * BS + wave * 32 + l32) * D;
@@ -557,6 +583,7 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(Geo g, const int32_t
 
 struct BwdWs {
   float* rowdot;    // [B, Hq, N]
+  float* lse2;      // [B, Hq, N]: lse * log2(e)
   int32_t* counts;  // [nkb]
   int32_t* list_off;  // [nkb + 1]
   int32_t* seg_off;   // [nkb + 1]
@@ -590,6 +617,7 @@ BwdWs carve_bwd(const Geo& g, void* base) {
   };
   BwdWs w;
   w.rowdot = (float*)take(sizeof(float) * (size_t)g.B * g.Hq * g.N);
+  w.lse2 = (float*)take(sizeof(float) * (size_t)g.B * g.Hq * g.N);
   w.counts = (int32_t*)take(sizeof(int32_t) * z.nkb);
   w.list_off = (int32_t*)take(sizeof(int32_t) * (z.nkb + 1));
   w.seg_off = (int32_t*)take(sizeof(int32_t) * (z.nkb + 1));
@@ -609,7 +637,7 @@ hipError_t launch_bwd_t(const Geo& g, const void* q, const void* k, const void* 
   const uint16_t* dot = (const uint16_t*)dout;
   const int64_t rows = (int64_t)g.B * g.Hq * g.N;
   hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, dot,
-                     (const uint16_t*)out, w.rowdot, rows);
+                     (const uint16_t*)out, lse, w.rowdot, w.lse2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // dQ: the forward's workgroup shape (8, 4, 2 or 1 waves per part)
@@ -633,7 +661,7 @@ hipError_t launch_bwd_t(const Geo& g, const void* q, const void* k, const void* 
                      w.list_off, w.lists, 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_kv_kernel<D, BS>), dim3((unsigned)z.max_segs), dim3(BS / 32 * 64), 0, s, g, qt, kt, vt, dot,
-                     lse, w.rowdot, w.lists, w.list_off, w.seg_off, (int)z.nkb, w.pdk, w.pdv);
+                     w.lse2, w.rowdot, w.lists, w.list_off, w.seg_off, (int)z.nkb, w.pdk, w.pdv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_kv_reduce_kernel<D>), dim3((unsigned)z.nkb), dim3(256), 0, s, g, w.seg_off, w.pdk, w.pdv,
                      (uint16_t*)dk, (uint16_t*)dv);
@@ -655,7 +683,7 @@ hipError_t launch_bwd_d(const Geo& g, const void* q, const void* k, const void* 
 
 size_t attn_bwd_workspace_bytes(const Geo& g) {
   const BwdSizes z = bwd_sizes(g);
-  return rnd(sizeof(float) * (size_t)g.B * g.Hq * g.N) + rnd(sizeof(int32_t) * z.nkb) +
+  return 2 * rnd(sizeof(float) * (size_t)g.B * g.Hq * g.N) + rnd(sizeof(int32_t) * z.nkb) +
          2 * rnd(sizeof(int32_t) * (z.nkb + 1)) + rnd(sizeof(int32_t) * z.max_entries) +
          2 * rnd(sizeof(float) * (size_t)z.max_segs * g.bs * g.D);
 }
