@@ -66,9 +66,21 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restr
 // ---------------------------------------------------------------------------
 // dQ: query-centric. A workgroup serves NW waves x 32 query rows of one
 // (batch, kv head, query block) unit and walks the unit's attended tiles as
-// the forward does. K is staged with the transposing-read pitch (it is read
-// both as rows, for S^T = K Q^T, and as columns, for dQ^T += K^T dS^T), V with
-// the row pitch (dP^T = V dO^T).
+// the forward does. V is staged at the row pitch (dP^T = V dO^T). K is read both
+// as rows (S^T = K Q^T) and as columns (dQ^T += K^T dS^T), and no padded pitch
+// serves both without bank conflicts: at D = 128 its rows are unpadded 256-byte
+// rows with the logical 16-byte unit u of row r at u ^ dq_swz(r), for which the
+// bank-conflict counter of gfx950 reads zero on both reads; at D = 64 they are
+// padded to the transposing pitch.
+
+template <int D, int BS>
+struct DqKLayout {
+  static constexpr bool kSwz = D == 128;
+  static constexpr int PITCH = kSwz ? D : TilePitch<D, BS>::V;  // elements per row
+  static constexpr int SIZE = kSwz ? BS * D : TilePitch<D, BS>::VSIZE;
+};
+
+__device__ __forceinline__ int dq_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
 template <int D, int BS>
 struct DqState {
@@ -77,16 +89,95 @@ struct DqState {
   f32x16_t acc[D / 32];
   float lse2;  // this lane's query: lse in log2 units (+inf for a row past the sequence)
   float rd;    // this lane's query: D_i
-  int offkt;   // transposing reads of the K tile
+  // byte offsets into a K tile: row fragment of step ds (row l32 of a 32-row
+  // block), transposing reads of slice db (rows of a 16-row block, first and
+  // second eight)
+  int offr[D / 16];
+  int offtl[D / 32], offtu[D / 32];
+  __device__ __forceinline__ void init_offsets(int lane) {
+    using KL = DqKLayout<D, BS>;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int rr = hi * 4 + ((lane & 15) >> 2);
+#pragma unroll
+    for (int ds = 0; ds < D / 16; ++ds) {
+      const int u = 2 * ds + hi;
+      offr[ds] = KL::kSwz ? (l32 * D + ((u ^ dq_swz(l32)) * 8)) * 2 : (l32 * KL::PITCH + u * 8) * 2;
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      if (KL::kSwz) {
+        offtl[db] = (rr * D + (((col >> 3) ^ dq_swz(rr)) * 8) + (col & 7)) * 2;
+        offtu[db] = ((rr + 8) * D + (((col >> 3) ^ dq_swz(rr + 8)) * 8) + (col & 7)) * 2;
+      } else {
+        offtl[db] = (rr * KL::PITCH + col) * 2;
+        offtu[db] = ((rr + 8) * KL::PITCH + col) * 2;
+      }
+    }
+  }
 };
+
+// Per-lane source offsets of one wave's copies of a dQ stage: V rows at the row
+// pitch (the forward's K plan) and K rows in DqKLayout.
+template <int D, int BS, int NW>
+struct DqPlan {
+  using TP = TilePitch<D, BS>;
+  using KL = DqKLayout<D, BS>;
+  static constexpr int VN = (TP::KI + NW - 1) / NW;
+  static constexpr int KCOP = KL::SIZE / 512;  // whole 1 KB copies of the K tile
+  static constexpr int KN = (KCOP + NW - 1) / NW;
+  int v[VN];
+  int k[KN];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int n = 0; n < VN; ++n) v[n] = unit_src<D, TP::KU>((wave + NW * n) * 64 + lane, BS);
+#pragma unroll
+    for (int n = 0; n < KN; ++n) {
+      const int p = (wave + NW * n) * 64 + lane;
+      if (KL::kSwz) {
+        const int r = p / (D / 8);
+        k[n] = r * D + (((p % (D / 8)) ^ dq_swz(r)) * 8);
+      } else {
+        k[n] = unit_src<D, TP::VU>(p, BS);
+      }
+    }
+  }
+};
+
+// Issue the copies of one dQ stage: V tile vt into vdst (row pitch), K tile kt
+// into kdst (DqKLayout). Rows past `rows_in_mem` re-read the last valid row.
+template <int D, int BS, int NW>
+__device__ __forceinline__ void issue_dq_tile(const uint16_t* __restrict__ vt, const uint16_t* __restrict__ kt,
+                                              int rows_in_mem, uint16_t* vdst, uint16_t* kdst, int wave, int lane,
+                                              const DqPlan<D, BS, NW>& plan) {
+  using PL = DqPlan<D, BS, NW>;
+  const int last = (rows_in_mem - 1) * D;
+#pragma unroll
+  for (int n = 0; n < PL::VN; ++n) {
+    const int i = wave + NW * n;
+    if (i < TilePitch<D, BS>::KI) {
+      const int off = min(plan.v[n], last + (plan.v[n] & (D - 1)));
+      __builtin_amdgcn_global_load_lds(vt + off, (lds_void_ptr)(vdst + i * 512), 16, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < PL::KN; ++n) {
+    const int i = wave + NW * n;
+    if (i < PL::KCOP) {
+      const int off = min(plan.k[n], last + (plan.k[n] & (D - 1)));
+      __builtin_amdgcn_global_load_lds(kt + off, (lds_void_ptr)(kdst + i * 512), 16, 0, 0);
+    }
+  }
+}
 
 template <int D, int BS>
 __device__ __forceinline__ void dq_tile(DqState<D, BS>& st, const uint16_t* ks, const uint16_t* vs, int nvalid,
                                         bool local, int key0, int qpos, int l32, int hi, float c, int wg_qmax) {
   constexpr int NDS = D / 16, NDB = D / 32;
-  constexpr int KC = BS < 64 ? BS : 64;
+  // keys per chunk: 32 when the K tile carries per-lane offset tables (register room)
+  constexpr int KC = DqKLayout<D, BS>::kSwz ? 32 : (BS < 64 ? BS : 64);
   constexpr int NKB = KC / 32;
-  constexpr int PK = TilePitch<D, BS>::K, PV = TilePitch<D, BS>::V;
+  constexpr int PK = TilePitch<D, BS>::K, KP = DqKLayout<D, BS>::PITCH;
 #pragma unroll
   for (int ch = 0; ch < BS / KC; ++ch) {
     if (ch > 0 && (ch * KC >= nvalid || (local && key0 + ch * KC > wg_qmax))) break;
@@ -98,7 +189,9 @@ __device__ __forceinline__ void dq_tile(DqState<D, BS>& st, const uint16_t* ks, 
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
         const int row = ch * KC + kb * 32 + l32, col = ds * 16 + hi * 8;
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<PV>(ks, row, col), st.qf[ds], s[kb], 0, 0, 0);
+        const bf16x8_t kfr = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const char*>(ks) +
+                                                                (ch * KC + kb * 32) * KP * 2 + st.offr[ds]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, st.qf[ds], s[kb], 0, 0, 0);
         dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<PK>(vs, row, col), st.df[ds], dp[kb], 0, 0, 0);
       }
     }
@@ -119,10 +212,15 @@ __device__ __forceinline__ void dq_tile(DqState<D, BS>& st, const uint16_t* ks, 
         bf16x8_t b;
 #pragma unroll
         for (int e = 0; e < 8; ++e) b[e] = (__bf16)s[kb][hh * 8 + e];
+        const char* kr = reinterpret_cast<const char*>(ks) + (ch * KC + kb * 32 + hh * 16) * KP * 2;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<PV>(ks, st.offkt, ch * KC + kb * 32 + hh * 16, db),
-                                                               b, st.acc[db], 0, 0, 0);
+        for (int db = 0; db < NDB; ++db) {
+          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(kr + st.offtl[db]));
+          const v4i16_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(kr + st.offtu[db]));
+          const v4i16_t a8[2] = {lo, up};
+          st.acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a8), b, st.acc[db], 0, 0,
+                                                               0);
+        }
       }
   }
 }
@@ -140,11 +238,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(Geo g, const uint16_t* 
   constexpr int NT = NW * 64;
   constexpr int NDS = D / 16, NDB = D / 32;
   using TP = TilePitch<D, BS>;
-  // stage s: V rows at the row pitch (VS*), K at the transposing pitch (KS*)
+  // stage s: V rows at the row pitch (VS*), K in the layout DqKLayout (KS*)
   __shared__ __attribute__((aligned(16))) uint16_t VS0[TP::KSIZE];
-  __shared__ __attribute__((aligned(16))) uint16_t KS0[TP::VSIZE];
+  __shared__ __attribute__((aligned(16))) uint16_t KS0[DqKLayout<D, BS>::SIZE];
   __shared__ __attribute__((aligned(16))) uint16_t VS1[TP::KSIZE];
-  __shared__ __attribute__((aligned(16))) uint16_t KS1[TP::VSIZE];
+  __shared__ __attribute__((aligned(16))) uint16_t KS1[DqKLayout<D, BS>::SIZE];
   __shared__ int sel[kMaxTopK];
 
   const int slabs = g.B * g.Hkv;
@@ -183,7 +281,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(Geo g, const uint16_t* 
     for (int i = 0; i < 16; ++i) st.acc[db][i] = 0.f;
   st.lse2 = qvalid ? lse[row] * kLog2e : __builtin_inff();
   st.rd = qvalid ? rowdot[row] : 0.f;
-  st.offkt = tr_offset<TP::V>(lane);
+  st.init_offsets(lane);
   const float c = g.scale * kLog2e;
   const int wg_qmax = qb * BS + (((part + 1) * NW - 1) / g.G) * 32 + 31;
 
@@ -191,30 +289,30 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(Geo g, const uint16_t* 
   const uint16_t* vbase = v + ((int64_t)b * g.Hkv + kvh) * g.N * D;
   __syncthreads();
   const TileWalk walk = make_walk(g, qb, sel, nsel);
-  DmaPlan<D, BS, NW> plan;
+  DqPlan<D, BS, NW> plan;
   plan.init(wave, lane);
 
   int j, nvalid;
   bool local;
   walk.at(0, sel, g, qb, local_rows, j, nvalid, local);
-  issue_tile<D, BS, NW>(vbase + (int64_t)j * BS * D, kbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), VS0, KS0,
-                        wave, lane, plan);
+  issue_dq_tile<D, BS, NW>(vbase + (int64_t)j * BS * D, kbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), VS0, KS0,
+                           wave, lane, plan);
   for (int t = 0; t < walk.ntiles; t += 2) {
     wait_loads_and_sync();
     int j1 = 0, nv1 = 0;
     bool loc1 = false;
     if (t + 1 < walk.ntiles) {
       walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
-      issue_tile<D, BS, NW>(vbase + (int64_t)j1 * BS * D, kbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), VS1,
-                            KS1, wave, lane, plan);
+      issue_dq_tile<D, BS, NW>(vbase + (int64_t)j1 * BS * D, kbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS),
+                               VS1, KS1, wave, lane, plan);
     }
     dq_tile<D, BS>(st, KS0, VS0, nvalid, local, j * BS, qpos, l32, hi, c, wg_qmax);
     if (t + 1 >= walk.ntiles) break;
     wait_loads_and_sync();
     if (t + 2 < walk.ntiles) {
       walk.at(t + 2, sel, g, qb, local_rows, j, nvalid, local);
-      issue_tile<D, BS, NW>(vbase + (int64_t)j * BS * D, kbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), VS0,
-                            KS0, wave, lane, plan);
+      issue_dq_tile<D, BS, NW>(vbase + (int64_t)j * BS * D, kbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), VS0,
+                               KS0, wave, lane, plan);
     }
     dq_tile<D, BS>(st, KS1, VS1, nv1, loc1, j1 * BS, qpos, l32, hi, c, wg_qmax);
   }
@@ -333,85 +431,164 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: key-centric. A workgroup serves one segment of one key block's list;
-// wave w owns keys [32 w, 32 w + 32) of the block and keeps their K and V rows
-// as matrix operands. For every (query block, head) of the segment the query
-// rows and their output gradients are staged in LDS (Q at the row pitch, dO at
-// the transposing pitch) and
-//   S = Q K^T, dP = dO V^T (lane = key), p, dS,
-//   dV^T += dO^T p, dK^T += Q^T dS   (d x keys, lane = key).
+// dK, dV: key-centric. A workgroup of BS/16 waves serves one segment of one key
+// block's list; wave w owns keys [16 w, 16 w + 16) of the block and keeps their
+// K and V rows as the B operands of 16x16x32 matrix products (lane = key), so
+// that its state leaves room for two waves per SIMD. For every (query block,
+// head) of the segment the query rows Q and their output gradients dO are
+// staged in LDS, and per 32-row chunk
+//   S = Q K^T, dP = dO V^T   (rows = queries, lane = key),
+//   p = exp2(S c - lse2), dS = p (dP - D),
+//   dV^T += dO^T p, dK^T += Q^T dS   (rows = d, lane = key).
+// The 32 query rows of a chunk enter the second pair of products in the order
+// the first pair leaves them in the lanes: slot j of lane group g is row
+// 4 g + j for j < 4 and row 16 + 4 g + j - 4 after, and the transposing reads of
+// Q and dO take their rows in the same order.
+//
+// Tiles are unpadded, D/8 16-byte units per row, with the logical unit u of row
+// r stored at u ^ kv_swz(r). In product step ds of S and dP, lane group g
+// (lanes 16 g to 16 g + 15) takes the row unit (D/32) g + ds: the contraction
+// over d visits the columns in that order, on both operands. With this layout
+// the bank-conflict counter of gfx950 reads zero for the row fragments (16 rows
+// at one unit per lane group) and for the transposing reads (4 rows x 32 bytes
+// per lane group) at D = 128 and D = 64; with adjacent units per lane group
+// instead, the row fragments conflict whatever the swizzle. D = 128: r mod 8 = k
+// maps to 2k, plus one for the rows 4-7 of the first eight and 0-3 of the next.
+// D = 64 (128-byte rows): 2k mod 8, XOR 3 for k >= 4, XOR 1 for the second eight
+// rows.
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+  const int k = r & 7, h = (r >> 3) & 1;
+  if constexpr (D == 128) return 2 * k + ((k >> 2) ^ h);
+  else return ((2 * k) & 7) ^ (3 * (k >> 2)) ^ h;
+}
+
+// Per-lane source offsets (elements, row * D + col) of this wave's copies of a
+// swizzled tile; NC copies of 64 units each.
+template <int D, int BS, int NW>
+struct KvPlan {
+  static constexpr int UPR = D / 8;
+  static constexpr int NC = BS * UPR / 64 / NW;
+  int src[NC];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+      const int p = (wave + NW * n) * 64 + lane;  // physical unit of the tile
+      const int r = p / UPR;
+      src[n] = r * D + (((p % UPR) ^ kv_swz<D>(r)) * 8);
+    }
+  }
+};
+
+// Issue the copies of one (query block, head) stage: Q and dO rows (swizzled),
+// and the rows' lse2 and D (64 floats per wave instruction). Rows past the
+// sequence re-read the last row; they are masked by `rows`.
+template <int D, int BS, int NW>
+__device__ __forceinline__ void issue_kv_rows(const Geo& g, const uint16_t* q, const uint16_t* dout,
+                                              const float* lse2, const float* rowdot, int b, int h, int qb,
+                                              uint16_t* qdst, uint16_t* odst, float* ldst, float* rdst, int wave,
+                                              int lane, const KvPlan<D, BS, NW>& plan) {
+  using PL = KvPlan<D, BS, NW>;
+  const int64_t r0 = ((int64_t)b * g.Hq + h) * g.N + (int64_t)qb * BS;
+  const int rows = min(BS, g.N - qb * BS);
+  const int last = (rows - 1) * D;
+  const uint16_t* qt = q + r0 * D;
+  const uint16_t* ot = dout + r0 * D;
+#pragma unroll
+  for (int n = 0; n < PL::NC; ++n) {
+    const int off = min(plan.src[n], last + (plan.src[n] & (D - 1)));
+    const int i = wave + NW * n;
+    __builtin_amdgcn_global_load_lds(qt + off, (lds_void_ptr)(qdst + i * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(ot + off, (lds_void_ptr)(odst + i * 512), 16, 0, 0);
+  }
+#pragma unroll
+  for (int n = 0; n < (BS + 63) / 64; ++n) {
+    if (n % NW == wave) {
+      const int r = min(n * 64 + lane, rows - 1);
+      __builtin_amdgcn_global_load_lds(lse2 + r0 + r, (lds_void_ptr)(ldst + n * 64), 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(rowdot + r0 + r, (lds_void_ptr)(rdst + n * 64), 4, 0, 0);
+    }
+  }
+}
+
+// Transposed fragment of a swizzled tile: rows (queries) 4 g + [0, 4) and
+// 16 + 4 g + [0, 4) from row q0, columns [16 db, 16 db + 16), as the A operand
+// (columns become rows) of a 16x16x32 product; `off` is this lane's byte offset
+// for db (row 4 g + lane%16/4, its piece lane%4 of the 16-column slice).
+template <int D>
+__device__ __forceinline__ bf16x8_t kv_tr_frag(const uint16_t* tile, int off, int q0) {
+  const char* base = reinterpret_cast<const char*>(tile) + q0 * D * 2 + off;
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
+  const v4i16_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 16 * D * 2));
+  const v4i16_t a8[2] = {lo, up};
+  return __builtin_bit_cast(bf16x8_t, a8);
+}
 
 template <int D, int BS>
-__device__ __forceinline__ void kv_tile(const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
-                                        f32x16_t (&dk)[D / 32], f32x16_t (&dv)[D / 32], const uint16_t* qs,
+__device__ __forceinline__ void kv_tile(const bf16x8_t (&kf)[D / 32], const bf16x8_t (&vf)[D / 32],
+                                        f32x4_t (&dk)[D / 16], f32x4_t (&dv)[D / 16], const uint16_t* qs,
                                         const uint16_t* os, const float* ls, const float* rs, bool mask, int rows,
-                                        int rlo, int l32, int hi, int offq, int offo, float c) {
-  constexpr int NDS = D / 16, NDB = D / 32;
-  constexpr int QC = 32;  // query rows per chunk (one 32-row block keeps the registers in bounds)
-  constexpr int PK = TilePitch<D, BS>::K, PV = TilePitch<D, BS>::V;
+                                        int rlo, int g4, const int (&offr)[D / 32], const int (&offt)[D / 16],
+                                        float c) {
+  constexpr int NDS = D / 32, NDB = D / 16;
+  constexpr int QC = 32;
 #pragma unroll
   for (int ch = 0; ch < BS / QC; ++ch) {
     if (ch > 0 && ch * QC >= rows) break;
-    f32x16_t s, dp;
+    const int q0 = ch * QC;
+    f32x4_t s[2], dp[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-    // every LDS fragment of the chunk is requested before its first product: with
-    // one wave per SIMD nothing else hides the LDS latency
-    bf16x8_t fq[NDS], fo[NDS], tv[2][NDB], tq[2][NDB];
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      const int row = ch * QC + l32, col = ds * 16 + hi * 8;
-      fq[ds] = row_frag<PK>(qs, row, col);
-      fo[ds] = row_frag<PV>(os, row, col);
-    }
+      for (int i = 0; i < 4; ++i) s[mb][i] = dp[mb][i] = 0.f;
+    bf16x8_t fq[2][NDS], fo[2][NDS];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        tv[hh][db] = tr_frag<PV>(os, offo, ch * QC + hh * 16, db);
-        tq[hh][db] = tr_frag<PK>(qs, offq, ch * QC + hh * 16, db);
+      for (int ds = 0; ds < NDS; ++ds) {
+        const int o = (q0 + 16 * mb) * D * 2 + offr[ds];
+        fq[mb][ds] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const char*>(qs) + o);
+        fo[mb][ds] = *reinterpret_cast<const bf16x8_t*>(reinterpret_cast<const char*>(os) + o);
       }
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[ds], kf[ds], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo[ds], vf[ds], dp, 0, 0, 0);
-    }
-    // element i is query row r = ch*QC + (i/4)*8 + hi*4 + i%4; ls holds lse in
-    // log2 units
+    for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const float4 l4 = *reinterpret_cast<const float4*>(ls + ch * QC + i4 * 8 + hi * 4);
+      for (int mb = 0; mb < 2; ++mb) {
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fq[mb][ds], kf[ds], s[mb], 0, 0, 0);
+        dp[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fo[mb][ds], vf[ds], dp[mb], 0, 0, 0);
+      }
+    // element i of block mb is query row q0 + 16 mb + 4 g4 + i
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int r0 = q0 + 16 * mb + 4 * g4;
+      const float4 l4 = *reinterpret_cast<const float4*>(ls + r0);
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[i4 * 4 + e] = fast_exp2(fmaf(s[i4 * 4 + e], c, -lv[e]));
-    }
-    if (mask) {  // uniform: only partial-sink, causal and ragged tiles; rows [rlo, rows) count for this key
+      for (int i = 0; i < 4; ++i) s[mb][i] = fast_exp2(fmaf(s[mb][i], c, -lv[i]));
+      if (mask) {  // uniform: partial-sink, causal and ragged tiles; rows [rlo, rows) count for this key
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = ch * QC + (i >> 2) * 8 + hi * 4 + (i & 3);
-        s[i] = r >= rlo && r < rows ? s[i] : 0.f;
+        for (int i = 0; i < 4; ++i) s[mb][i] = r0 + i >= rlo && r0 + i < rows ? s[mb][i] : 0.f;
       }
-    }
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const float4 d4 = *reinterpret_cast<const float4*>(rs + ch * QC + i4 * 8 + hi * 4);
+      const float4 d4 = *reinterpret_cast<const float4*>(rs + r0);
       const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dp[i4 * 4 + e] = s[i4 * 4 + e] * (dp[i4 * 4 + e] - dv4[e]);
+      for (int i = 0; i < 4; ++i) dp[mb][i] = s[mb][i] * (dp[mb][i] - dv4[i]);
+    }
+    bf16x8_t pb, sb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pb[i] = (__bf16)s[0][i];
+      pb[4 + i] = (__bf16)s[1][i];
+      sb[i] = (__bf16)dp[0][i];
+      sb[4 + i] = (__bf16)dp[1][i];
     }
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      bf16x8_t pb, sb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[e] = (__bf16)s[hh * 8 + e];
-        sb[e] = (__bf16)dp[hh * 8 + e];
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tv[hh][db], pb, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[hh][db], sb, dk[db], 0, 0, 0);
-      }
+    for (int db = 0; db < NDB; ++db) {
+      dv[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv_tr_frag<D>(os, offt[db], q0), pb, dv[db], 0, 0, 0);
+      dk[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv_tr_frag<D>(qs, offt[db], q0), sb, dk[db], 0, 0, 0);
     }
   }
 }
@@ -421,40 +598,20 @@ __device__ __forceinline__ void kv_tile(const bf16x8_t (&kf)[D / 16], const bf16
 // [rlo, rows): rlo = the key's own row on the causal diagonal, past the block
 // for a key outside the sink (partial sink tile) or the sequence.
 template <int D, int BS>
-__device__ __forceinline__ void kv_stage(const bf16x8_t (&kf)[D / 16], const bf16x8_t (&vf)[D / 16],
-                                         f32x16_t (&dk)[D / 32], f32x16_t (&dv)[D / 32], const uint16_t* qs,
+__device__ __forceinline__ void kv_stage(const bf16x8_t (&kf)[D / 32], const bf16x8_t (&vf)[D / 32],
+                                         f32x4_t (&dk)[D / 16], f32x4_t (&dv)[D / 16], const uint16_t* qs,
                                          const uint16_t* os, const float* ls, const float* rs, const Geo& g, int qb,
-                                         int kind, int j, int key, int l32, int hi, int offq, int offo, float c) {
+                                         int kind, int j, int key, int g4, const int (&offr)[D / 32],
+                                         const int (&offt)[D / 16], float c) {
   const int rows = min(BS, g.N - qb * BS);
   const bool mask = !(kind == kFull && rows == BS && (j + 1) * BS <= g.N);
   const bool key_ok = key < (kind == kSinkPart ? g.sink : g.N);
   const int rlo = !key_ok ? BS : kind == kLocal ? (key & (BS - 1)) : 0;
-  kv_tile<D, BS>(kf, vf, dk, dv, qs, os, ls, rs, mask, rows, rlo, l32, hi, offq, offo, c);
-}
-
-// Issue the copies of one (query block, head) stage: Q and dO rows, and the
-// rows' lse and D (64 floats per wave instruction; rows past the sequence
-// re-read the last row, they are masked by `rows`).
-template <int D, int BS, int NW>
-__device__ __forceinline__ void issue_rows(const Geo& g, const uint16_t* q, const uint16_t* dout, const float* lse,
-                                           const float* rowdot, int b, int h, int qb, uint16_t* qdst, uint16_t* odst,
-                                           float* ldst, float* rdst, int wave, int lane,
-                                           const DmaPlan<D, BS, NW>& plan) {
-  const int64_t r0 = ((int64_t)b * g.Hq + h) * g.N + (int64_t)qb * BS;
-  const int rows = min(BS, g.N - qb * BS);
-  issue_tile<D, BS, NW>(q + r0 * D, dout + r0 * D, rows, qdst, odst, wave, lane, plan);
-#pragma unroll
-  for (int n = 0; n < (BS + 63) / 64; ++n) {
-    if (n % NW == wave) {
-      const int r = min(n * 64 + lane, rows - 1);
-      __builtin_amdgcn_global_load_lds(lse + r0 + r, (lds_void_ptr)(ldst + n * 64), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(rowdot + r0 + r, (lds_void_ptr)(rdst + n * 64), 4, 0, 0);
-    }
-  }
+  kv_tile<D, BS>(kf, vf, dk, dv, qs, os, ls, rs, mask, rows, rlo, g4, offr, offt, c);
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(BS / 32 * 64) void bwd_kv_kernel(Geo g, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(BS / 16 * 64) void bwd_kv_kernel(Geo g, const uint16_t* __restrict__ q,
                                                               const uint16_t* __restrict__ k,
                                                               const uint16_t* __restrict__ v,
                                                               const uint16_t* __restrict__ dout,
@@ -464,14 +621,13 @@ __global__ __launch_bounds__(BS / 32 * 64) void bwd_kv_kernel(Geo g, const uint1
                                                               const int32_t* __restrict__ list_off,
                                                               const int32_t* __restrict__ seg_off, int nkb,
                                                               float* __restrict__ pdk, float* __restrict__ pdv) {
-  constexpr int NW = BS / 32;
-  constexpr int NDS = D / 16, NDB = D / 32;
-  constexpr int LS = BS < 64 ? 64 : BS;  // lse / D slots per stage (whole 64-float copies)
-  using TP = TilePitch<D, BS>;
-  __shared__ __attribute__((aligned(16))) uint16_t Q0[TP::KSIZE];
-  __shared__ __attribute__((aligned(16))) uint16_t O0[TP::VSIZE];
-  __shared__ __attribute__((aligned(16))) uint16_t Q1[TP::KSIZE];
-  __shared__ __attribute__((aligned(16))) uint16_t O1[TP::VSIZE];
+  constexpr int NW = BS / 16;
+  constexpr int NDS = D / 32, NDB = D / 16;
+  constexpr int LS = BS < 64 ? 64 : BS;  // lse2 / D slots per stage (whole 64-float copies)
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t O0[BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Q1[BS * D];
+  __shared__ __attribute__((aligned(16))) uint16_t O1[BS * D];
   __shared__ __attribute__((aligned(16))) float L0[LS], R0[LS], L1[LS], R1[LS];
 
   const int w = blockIdx.x;
@@ -492,25 +648,38 @@ __global__ __launch_bounds__(BS / 32 * 64) void bwd_kv_kernel(Geo g, const uint1
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int l32 = lane & 31;
-  const int hi = lane >> 5;
-  const int key = j * BS + wave * 32 + l32;
+  const int n16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int key = j * BS + wave * 16 + n16;
   const int64_t krow = ((int64_t)b * g.Hkv + kvh) * g.N + min(key, g.N - 1);
+  // K and V rows as B operands: key n16, in step ds the columns of unit
+  // NDS g4 + ds, [8 (NDS g4 + ds), + 8)
   bf16x8_t kf[NDS], vf[NDS];
 #pragma unroll
   for (int ds = 0; ds < NDS; ++ds) {
-    kf[ds] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(k + krow * D + ds * 16 + hi * 8));
-    vf[ds] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(v + krow * D + ds * 16 + hi * 8));
+    const int col = (NDS * g4 + ds) * 8;
+    kf[ds] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(k + krow * D + col));
+    vf[ds] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(v + krow * D + col));
   }
-  f32x16_t dk[NDB], dv[NDB];
+  f32x4_t dk[NDB], dv[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dk[db][i] = dv[db][i] = 0.f;
-  const int offq = tr_offset<TP::K>(lane);
-  const int offo = tr_offset<TP::V>(lane);
+    for (int i = 0; i < 4; ++i) dk[db][i] = dv[db][i] = 0.f;
+  // LDS byte offsets: row fragments (row n16 of a 16-row block, logical unit
+  // NDS g4 + ds) and transposing reads (row 4 g4 + n16/4, piece n16%4 of the
+  // 16-column slice db); the swizzle depends on the row mod 16 only
+  int offr[NDS], offt[NDB];
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) offr[ds] = (n16 * D + (((NDS * g4 + ds) ^ kv_swz<D>(n16)) * 8)) * 2;
+  {
+    const int rr = 4 * g4 + (n16 >> 2), cc = n16 & 3;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      offt[db] = (rr * D + (((2 * db + (cc >> 1)) ^ kv_swz<D>(rr)) * 8)) * 2 + (cc & 1) * 8;
+  }
   const float c = g.scale * kLog2e;
-  DmaPlan<D, BS, NW> plan;
+  KvPlan<D, BS, NW> plan;
   plan.init(wave, lane);
 
   auto entry = [&](int t, int& qb, int& h, int& kind) {
@@ -519,36 +688,36 @@ __global__ __launch_bounds__(BS / 32 * 64) void bwd_kv_kernel(Geo g, const uint1
     kind = e >> 28;
     h = kvh * g.G + t % g.G;
   };
+
   int qb, h, kind;
   entry(0, qb, h, kind);
-  issue_rows<D, BS, NW>(g, q, dout, lse2, rowdot, b, h, qb, Q0, O0, L0, R0, wave, lane, plan);
+  issue_kv_rows<D, BS, NW>(g, q, dout, lse2, rowdot, b, h, qb, Q0, O0, L0, R0, wave, lane, plan);
   for (int t = 0; t < npairs; t += 2) {
     wait_loads_and_sync();
     int qb1 = 0, h1 = 0, kind1 = 0;
     if (t + 1 < npairs) {
       entry(t + 1, qb1, h1, kind1);
-      issue_rows<D, BS, NW>(g, q, dout, lse2, rowdot, b, h1, qb1, Q1, O1, L1, R1, wave, lane, plan);
+      issue_kv_rows<D, BS, NW>(g, q, dout, lse2, rowdot, b, h1, qb1, Q1, O1, L1, R1, wave, lane, plan);
     }
-    kv_stage<D, BS>(kf, vf, dk, dv, Q0, O0, L0, R0, g, qb, kind, j, key, l32, hi, offq, offo, c);
+    kv_stage<D, BS>(kf, vf, dk, dv, Q0, O0, L0, R0, g, qb, kind, j, key, g4, offr, offt, c);
     if (t + 1 >= npairs) break;
     wait_loads_and_sync();
     if (t + 2 < npairs) {
       entry(t + 2, qb, h, kind);
-      issue_rows<D, BS, NW>(g, q, dout, lse2, rowdot, b, h, qb, Q0, O0, L0, R0, wave, lane, plan);
+      issue_kv_rows<D, BS, NW>(g, q, dout, lse2, rowdot, b, h, qb, Q0, O0, L0, R0, wave, lane, plan);
     }
-    kv_stage<D, BS>(kf, vf, dk, dv, Q1, O1, L1, R1, g, qb1, kind1, j, key, l32, hi, offq, offo, c);
+    kv_stage<D, BS>(kf, vf, dk, dv, Q1, O1, L1, R1, g, qb1, kind1, j, key, g4, offr, offt, c);
   }
-  // partial sums of this segment: [segment][key of the block][d], fp32
-  float* pk = pdk + ((int64_t)w * BS + wave * 32 + l32) * D;
-  float* pv = pdv + ((int64_t)w * BS + wave * 32 + l32) * D;
+  // partial sums of this segment: [segment][key of the block][d], fp32; lane
+  // holds key n16, columns 16 db + 4 g4 + [0, 4)
+  float* pk = pdk + ((int64_t)w * BS + wave * 16 + n16) * D;
+  float* pv = pdv + ((int64_t)w * BS + wave * 16 + n16) * D;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; i += 4) {
-      const int d = db * 32 + (i >> 2) * 8 + hi * 4;
-      *reinterpret_cast<float4*>(pk + d) = make_float4(dk[db][i], dk[db][i + 1], dk[db][i + 2], dk[db][i + 3]);
-      *reinterpret_cast<float4*>(pv + d) = make_float4(dv[db][i], dv[db][i + 1], dv[db][i + 2], dv[db][i + 3]);
-    }
+  for (int db = 0; db < NDB; ++db) {
+    const int d = db * 16 + g4 * 4;
+    *reinterpret_cast<float4*>(pk + d) = make_float4(dk[db][0], dk[db][1], dk[db][2], dk[db][3]);
+    *reinterpret_cast<float4*>(pv + d) = make_float4(dv[db][0], dv[db][1], dv[db][2], dv[db][3]);
+  }
 }
 
 // dK = scale * (sum of the segments' partial sums), dV = sum, in segment order.
@@ -660,7 +829,7 @@ hipError_t launch_bwd_t(const Geo& g, const void* q, const void* k, const void* 
   hipLaunchKernelGGL(bwd_list_kernel, dim3((unsigned)z.nkb), dim3(kListThreads), 0, s, g, idx, cnt, w.counts,
                      w.list_off, w.lists, 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_kv_kernel<D, BS>), dim3((unsigned)z.max_segs), dim3(BS / 32 * 64), 0, s, g, qt, kt, vt, dot,
+  hipLaunchKernelGGL((bwd_kv_kernel<D, BS>), dim3((unsigned)z.max_segs), dim3(BS / 16 * 64), 0, s, g, qt, kt, vt, dot,
                      w.lse2, w.rowdot, w.lists, w.list_off, w.seg_off, (int)z.nkb, w.pdk, w.pdv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_kv_reduce_kernel<D>), dim3((unsigned)z.nkb), dim3(256), 0, s, g, w.seg_off, w.pdk, w.pdv,
