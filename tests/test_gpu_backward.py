@@ -37,6 +37,10 @@ CASES = {
     "d128_bs32": (P(1, 4, 2, 1000, 128, 32, 2, 4, 5, 32, "bf16"), ("log_distance", 8)),
     "k0": (P(1, 4, 2, 1500, 128, 64, 4, 2, 0, 64, "bf16"), None),
     "shorter_than_block": (P(1, 2, 1, 50, 128, 64, 4, 2, 4, 64, "bf16"), None),
+    # d = 64 at blocks 128 and 64 (the key-centric swizzle over several 32-row
+    # chunks and 8 or 4 waves); an odd group (the query-centric pass at 2 waves)
+    "d64_bs128_ragged": (P(1, 4, 2, 3100, 64, 128, 4, 3, 4, 64, "bf16"), ("uniform_pairs", 4)),
+    "d64_bs64_group3": (P(1, 6, 2, 2500, 64, 64, 4, 2, 5, 64, "bf16"), ("uniform_pairs", 4)),
 }
 
 
