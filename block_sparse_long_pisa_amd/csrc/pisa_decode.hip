@@ -410,6 +410,12 @@ static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, c
     else if (e <= 4)
       hipLaunchKernelGGL((decode_select_kernel<T, D, 4>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
                          len_all, ws.idx, ws.cnt);
+    else if (e <= 5)  // K = 32 at fanout 8: 263 slots (the ranking's bit counts run over fewer slot groups)
+      hipLaunchKernelGGL((decode_select_kernel<T, D, 5>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+                         len_all, ws.idx, ws.cnt);
+    else if (e <= 6)
+      hipLaunchKernelGGL((decode_select_kernel<T, D, 6>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+                         len_all, ws.idx, ws.cnt);
     else if (e <= 8)
       hipLaunchKernelGGL((decode_select_kernel<T, D, 8>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
                          len_all, ws.idx, ws.cnt);

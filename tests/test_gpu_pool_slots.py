@@ -2,7 +2,7 @@
 
 The per-wave descent gives each lane ceil(pool / 64) pool slots, rounded up to
 one of the instantiated counts (1-6, 8, 10, 12, 16), and the decode descent
-rounds to 2, 4, 8 or 16. The top-K search skips slot groups past a level's
+rounds to 2, 4, 5, 6, 8 or 16. The top-K search skips slot groups past a level's
 pool. These cases choose K with fanout 8, so that the level-0 pool K*8 + 7
 lands in every slot count, and check every selection bit for bit against the
 oracle. The ragged last block (27 rows) also takes the query mean's general
@@ -48,7 +48,7 @@ def test_selection_for_each_pool_slot_count(K):
 
 
 # decode: K -> slots per lane of the workgroup descent
-DECODE_K = {8: 2, 24: 4, 56: 8, 120: 16}
+DECODE_K = {8: 2, 24: 4, 32: 5, 40: 6, 56: 8, 120: 16}
 
 
 @pytest.mark.parametrize("K", list(DECODE_K))
