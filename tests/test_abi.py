@@ -72,6 +72,8 @@ def test_layout_offsets(lib):
     (dict(levels=9), EUNSUP),
     (dict(top_k=-1), ESHAPE),
     (dict(top_k=300), EUNSUP),
+    (dict(top_k=257, fanout=2), EUNSUP),  # one past the largest kept set
+    (dict(top_k=256, fanout=4), EUNSUP),  # level-0 pool 1027 > 1024
     (dict(top_k=128, fanout=16), EUNSUP),
     (dict(sink_len=-1), ESHAPE),
     (dict(causal=2), EUNSUP),
@@ -90,6 +92,19 @@ def test_invalid_problems_are_rejected_on_the_host(lib, kw, status):
     assert lib.pisa_sparse_attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None) == status
     n = ctypes.c_size_t(0)
     assert lib.pisa_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(top_k=256, fanout=2, levels=8, block_size=32, seq_len=8192),  # largest kept set, deepest pyramid
+    dict(top_k=255, fanout=4, levels=3, seq_len=65536),                # level-0 pool of 1023 slots
+])
+def test_problems_at_the_limits_are_accepted(lib, kw):
+    p = _p(**kw)
+    offs = (ctypes.c_int64 * 16)()
+    assert lib.pisa_pyramid_layout(ctypes.byref(p), offs) == 0, lib.pisa_last_error()
+    n = ctypes.c_size_t(0)
+    assert lib.pisa_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value > 0
 
 
 def test_null_and_misaligned_pointers(lib):
