@@ -322,14 +322,20 @@ __device__ void block_descend(const Geo& g, const float* __restrict__ ps, int qb
     for (int w = 0; w < NWV; ++w) nvalid += sm.wcnt[w];
     const int nk = min(g.K, nvalid);
     if (nvalid > g.K) {  // score the pool; a level with at most K valid slots keeps them all
+      // slots without a node read a complete node of the pool (the first child of
+      // the first kept node, or at the top level the first node of the ancestor
+      // tail) so that no load is conditional; their scores are never used. A
+      // complete node is never written by the append of a token of this query's
+      // block, so that append may run beside this descent.
+      const int stand_in = nchild > 0 ? sm.kept[0] * g.f : anc_first;
       for (int base = 0; base < M; base += NG * U) {
         float4 x[U][DPL / 4];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int p = base + u * NG + grp;
           const int n = p < M ? sm.id[p] : INT_MAX;
-          // slots without a node read node 0 (always present) so that no load is conditional
-          const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)(n != INT_MAX ? n : 0) * D + sub * DPL);
+          const float4* row =
+              reinterpret_cast<const float4*>(lvl + (int64_t)(n != INT_MAX ? n : stand_in) * D + sub * DPL);
 #pragma unroll
           for (int e4 = 0; e4 < DPL / 4; ++e4) x[u][e4] = row[e4];
         }

@@ -230,7 +230,12 @@ pisa_status pisa_decode_step_ragged(const pisa_problem* p, const void* q, const 
  * exactly new_lens[b] tokens. Other nodes are not written. A sequence with
  * old_lens[b] < 0, new_lens[b] > seq_len or old_lens[b] >= new_lens[b] is left
  * as it is. One workgroup per (batch, kv head): meant for the few tokens a
- * decode step appends; a long prompt is faster through pisa_build_pyramid. */
+ * decode step appends; a long prompt is faster through pisa_build_pyramid.
+ * Ordering: a decode at length n reads only complete nodes (wholly before the
+ * block of its token n - 1), and appending that token writes only incomplete
+ * ones, so the append of a step's token may be issued before or after that
+ * step's decode, on the same stream or beside it on another; the decode of the
+ * next step must follow it. */
 pisa_status pisa_pyramid_append(const pisa_problem* p, const void* k_cache, float* pyramid, const int32_t* old_lens,
                                 const int32_t* new_lens, hipStream_t stream);
 

@@ -8,7 +8,9 @@ cache lengths, and the pyramid kept up to date as tokens are appended.
   bit for bit, the oracle's pyramid of exactly that many tokens; every node the
   append does not reach keeps its old value;
 * a short serving loop (append the new token, update the pyramid, decode) checked
-  step by step against the oracle.
+  step by step against the oracle;
+* the append of a step run before, after and beside that step's decode: the same
+  results bit for bit.
 """
 
 import math
@@ -186,3 +188,65 @@ def test_serving_loop_append_then_decode():
         for b, n in enumerate(lens):
             _check_prefix_pyramid(p, levels, kh, b, n)
         log(f"  step {s}: lengths {lens}, max abs err {err:.2e}")
+
+
+def test_append_may_run_beside_the_decode_of_its_step():
+    """The decode at length n scores only complete pyramid nodes, and the append
+    of its token n - 1 writes only that token's leaf and its ancestors, none of
+    them complete: so the append of a step may run after, or beside, that step's
+    decode (the next decode must follow it). Three orders of the same loop --
+    append then decode, decode then append, and the append on a second stream
+    beside the decode -- give the same results bit for bit, with lengths that
+    cross block boundaries."""
+    import block_sparse_long_pisa_amd as pisa
+
+    p = P(4, 8, 2, 1200, 128, 64, 4, 3, 4, 64, "bf16", decode=True)
+    start = [62, 127, 640, 1190]
+    steps = 4
+    q, k, v, _ = gen.host_decode_inputs(p, 93, _scale(p), p.seq_len)
+    cp = cprob(p)
+    rng = np.random.default_rng(5)
+    qs = [to_dev(gen.round_to_bf16((rng.standard_normal((p.batch, p.heads_q, p.head_dim)) /
+                                    math.sqrt(p.head_dim)).astype(np.float32)), p.dtype) for _ in range(steps)]
+    lens = [[n + s for n in start] for s in range(steps + 1)]
+    lens_d = [torch.tensor(l, dtype=torch.int32, device="cuda") for l in lens]
+    kd, vd = to_dev(k, p.dtype), to_dev(v, p.dtype)  # every token's key and value already in the cache
+
+    def run(order):
+        # a build over the whole capacity: the nodes a decode reads (complete ones)
+        # are exact, and each append brings its token's nodes to the prefix state
+        pyr = pisa.build_pyramid(cp, kd)
+        ws = torch.empty(max(1, pisa.decode_workspace_size(cp)), dtype=torch.uint8, device="cuda")
+        side = torch.cuda.Stream()
+        res = []
+        appended = torch.cuda.Event()
+        for s in range(steps):
+            if order == "append_first":
+                pisa.pyramid_append(cp, kd, pyr, lens_d[s], lens_d[s + 1])
+                r = pisa.decode_step_ragged(cp, qs[s], kd, vd, pyr, lens_d[s + 1], want_lse=True, want_idx=True,
+                                            workspace=ws)
+            elif order == "decode_first":
+                r = pisa.decode_step_ragged(cp, qs[s], kd, vd, pyr, lens_d[s + 1], want_lse=True, want_idx=True,
+                                            workspace=ws)
+                pisa.pyramid_append(cp, kd, pyr, lens_d[s], lens_d[s + 1])
+            else:  # the append on a second stream, beside the decode
+                main = torch.cuda.current_stream()
+                side.wait_stream(main)
+                with torch.cuda.stream(side):
+                    pisa.pyramid_append(cp, kd, pyr, lens_d[s], lens_d[s + 1])
+                    appended.record(side)
+                r = pisa.decode_step_ragged(cp, qs[s], kd, vd, pyr, lens_d[s + 1], want_lse=True, want_idx=True,
+                                            workspace=ws)
+                main.wait_event(appended)  # the next decode follows this append
+            res.append([to_host(x).copy() for x in r])
+        torch.cuda.synchronize()
+        return res, to_host(pyr)
+
+    a, pa = run("append_first")
+    b, pb = run("decode_first")
+    c, pc = run("beside")
+    assert np.array_equal(pa, pb) and np.array_equal(pa, pc)
+    for s in range(steps):
+        for x, y, z in zip(a[s], b[s], c[s]):
+            assert np.array_equal(x, y) and np.array_equal(x, z), f"step {s}"
+    log(f"  lengths {lens[0]} -> {lens[-1]}: three orders identical, counts {a[-1][3].reshape(-1).tolist()}")

@@ -166,6 +166,35 @@ def test_selection_ignores_blocks_after_the_query_block():
         assert descend([p[0, 0] for p in pyr3], qbar[0, 0, qb], qb, K, 0, bs, f) == base
 
 
+def test_decode_reads_no_pyramid_node_holding_its_own_token():
+    # A decode at length n scores only complete nodes, wholly before the block of
+    # its token n - 1; that token's append touches only its leaf and the leaf's
+    # ancestors, none of them complete. So the pyramid of the prefix without the
+    # token serves the decode as well, and a serving loop may run the append of a
+    # step beside that step's decode (lengths on and across block boundaries).
+    from oracle import decode_ragged
+
+    B, Hq, Hkv, cap, d, bs, f, L, K, s = 3, 4, 2, 1024, 16, 16, 4, 3, 5, 16
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    k = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, cap, d)).astype(np.float32)
+    most = 0
+    for lens in ((16 * 7 + 1, 16 * 8, 300), (16 * 8 + 1, 513, 1024), (17, 16, 1)):
+        before, after = k.copy(), k.copy()
+        for b, n in enumerate(lens):
+            before[b, :, n - 1:] = 0.0  # the prefix without the token
+            after[b, :, n:] = 0.0       # with it
+        pb, pa = build_pyramid(before, bs, f, L), build_pyramid(after, bs, f, L)
+        assert any(not np.array_equal(x, y) for x, y in zip(pb, pa))  # the appended token changes the pyramid
+        ob, lb, ib, cb = decode_ragged(q, after, v, pb, lens, K, s, bs, f, 0.25)
+        oa, la, ia, ca = decode_ragged(q, after, v, pa, lens, K, s, bs, f, 0.25)
+        assert np.array_equal(ib, ia) and np.array_equal(cb, ca)
+        assert np.array_equal(ob, oa) and np.array_equal(lb, la)
+        most = max(most, int(ca.max()))
+    assert most == K  # the longer sequences select a full set
+
+
 def test_equal_blocks_tie_to_lower_index():
     N, d, bs, f, L = 1024, 4, 16, 4, 3
     rng = np.random.default_rng(2)
