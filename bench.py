@@ -36,13 +36,13 @@ COPY_SCALE = {"fetch": 1048576.0 / 524332.9, "write": 1048576.0 / 1048576.0}
 MEASURED_TRAFFIC = {
     # step: (sources, sha256 prefix of their bytes in this order, FETCH_SIZE KiB, WRITE_SIZE KiB)
     "attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "5d3f16d4682ba197",
-                  5787617.8, 1048576.2),
+                  5789719.9, 1048577.7),
     "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "b7af1c49483bc6e8",
-                131123.5 + 338.0, 4608.2 + 72.0),  # leaf and levels 1, then levels 2 and up
-    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "5ab994057d218ca3",
-               526688.2, 1056.1),
-    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h"), "2c8e1d33bb0601d4",
-               47916.1 + 546819.6 + 5393.0, 80.0 + 9504.0 + 512.0),  # select + split attention + merge
+                131123.6 + 338.0, 4608.2 + 72.0),  # leaf and levels 1, then levels 2 and up
+    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "38953cc8efcc7328",
+               526688.2, 1056.2),
+    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h"), "d501bd409d649124",
+               47867.8 + 546818.9 + 5393.0, 80.1 + 9504.0 + 512.0),  # select + split attention + merge
 }
 
 
