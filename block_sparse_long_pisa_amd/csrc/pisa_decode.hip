@@ -400,6 +400,11 @@ static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, c
                                   int32_t* cnt_out, void* wsb, hipStream_t s) {
   const int splits = decode_splits(g, len_all);
   DecodeWs ws = carve(g, wsb, splits);
+  // the selection goes straight to the caller's buffers when they are given
+  // (the same layouts, [B * Hkv, K] and [B * Hkv]) and the attention reads it
+  // there: no copies after the step
+  if (idx_out != nullptr && g.K > 0) ws.idx = idx_out;
+  if (cnt_out != nullptr) ws.cnt = cnt_out;
   const int slabs = g.B * g.Hkv;
   {
     const int e = pool_slots_per_lane(g);
@@ -438,14 +443,7 @@ static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, c
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(g.B * g.Hq), dim3(D), 0, s, g, splits, ws, (T*)out, lse);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (idx_out != nullptr && g.K > 0) {
-    e = hipMemcpyAsync(idx_out, ws.idx, sizeof(int32_t) * slabs * g.K, hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return e;
-  }
-  if (cnt_out != nullptr) e = hipMemcpyAsync(cnt_out, ws.cnt, sizeof(int32_t) * slabs, hipMemcpyDeviceToDevice, s);
-  return e;
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr,

@@ -194,6 +194,9 @@ pisa_status pisa_decode_workspace_size(const pisa_problem* p, size_t* bytes);
  *   cache_len: 1..seq_len, the same for every sequence;
  *   out: [batch, heads_q, head_dim]; lse: nullable fp32 [batch, heads_q];
  *   idx_out: nullable int32 [batch, heads_kv, top_k]; cnt_out: nullable int32 [batch, heads_kv];
+ *            when given, the selection is written there and the attention of
+ *            the same call reads it back, so they must not overlap any other
+ *            buffer of the call;
  *   workspace: device memory of at least pisa_decode_workspace_size bytes.
  * Selection and attended set are those of a one-row query block at position
  * cache_len - 1. The attended blocks are split across workgroups and the
