@@ -620,7 +620,9 @@ __global__ __launch_bounds__(BS / 16 * 64) void bwd_kv_kernel(Geo g, const uint1
                                                               const int32_t* __restrict__ lists,
                                                               const int32_t* __restrict__ list_off,
                                                               const int32_t* __restrict__ seg_off, int nkb,
-                                                              float* __restrict__ pdk, float* __restrict__ pdv) {
+                                                              float* __restrict__ pdk, float* __restrict__ pdv,
+                                                              uint16_t* __restrict__ dkout,
+                                                              uint16_t* __restrict__ dvout) {
   constexpr int NW = BS / 16;
   constexpr int NDS = D / 32, NDB = D / 16;
   constexpr int LS = BS < 64 ? 64 : BS;  // lse2 / D slots per stage (whole 64-float copies)
@@ -708,8 +710,25 @@ __global__ __launch_bounds__(BS / 16 * 64) void bwd_kv_kernel(Geo g, const uint1
     }
     kv_stage<D, BS>(kf, vf, dk, dv, Q1, O1, L1, R1, g, qb1, kind1, j, key, g4, offr, offt, c);
   }
-  // partial sums of this segment: [segment][key of the block][d], fp32; lane
-  // holds key n16, columns 16 db + 4 g4 + [0, 4)
+  // lane holds key n16, columns 16 db + 4 g4 + [0, 4)
+  if (seg_off[kbid + 1] - seg_off[kbid] == 1) {
+    // the key block's only segment: dK and dV directly, as the reduce would
+    // write them (its sum starts from +0.0)
+    if (key < g.N) {
+      uint16_t* ok = dkout + ((int64_t)slab * g.N + key) * D;
+      uint16_t* ov = dvout + ((int64_t)slab * g.N + key) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = db * 16 + g4 * 4;
+        *reinterpret_cast<uint2*>(ok + d) = make_uint2(pack_bf16x2((0.f + dk[db][0]) * g.scale, (0.f + dk[db][1]) * g.scale),
+                                                       pack_bf16x2((0.f + dk[db][2]) * g.scale, (0.f + dk[db][3]) * g.scale));
+        *reinterpret_cast<uint2*>(ov + d) = make_uint2(pack_bf16x2(0.f + dv[db][0], 0.f + dv[db][1]),
+                                                       pack_bf16x2(0.f + dv[db][2], 0.f + dv[db][3]));
+      }
+    }
+    return;
+  }
+  // partial sums of this segment: [segment][key of the block][d], fp32
   float* pk = pdk + ((int64_t)w * BS + wave * 16 + n16) * D;
   float* pv = pdv + ((int64_t)w * BS + wave * 16 + n16) * D;
 #pragma unroll
@@ -720,7 +739,9 @@ __global__ __launch_bounds__(BS / 16 * 64) void bwd_kv_kernel(Geo g, const uint1
   }
 }
 
-// dK = scale * (sum of the segments' partial sums), dV = sum, in segment order.
+// dK = scale * (sum of the segments' partial sums), dV = sum, in segment order,
+// for the key blocks of more than one segment (the key-centric kernel writes a
+// single segment's block itself).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(Geo g, const int32_t* __restrict__ seg_off,
                                                             const float* __restrict__ pdk,
@@ -730,6 +751,7 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(Geo g, const int32_t
   const int slab = kbid / g.nb;
   const int j = kbid % g.nb;
   const int s0 = seg_off[kbid], s1 = seg_off[kbid + 1];
+  if (s1 - s0 == 1) return;
   const int rows = min(g.bs, g.N - j * g.bs);
   for (int e = threadIdx.x * 4; e < rows * D; e += 256 * 4) {
     const int r = e / D, d = e % D;
@@ -830,7 +852,8 @@ hipError_t launch_bwd_t(const Geo& g, const void* q, const void* k, const void* 
                      w.list_off, w.lists, 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_kv_kernel<D, BS>), dim3((unsigned)z.max_segs), dim3(BS / 16 * 64), 0, s, g, qt, kt, vt, dot,
-                     w.lse2, w.rowdot, w.lists, w.list_off, w.seg_off, (int)z.nkb, w.pdk, w.pdv);
+                     w.lse2, w.rowdot, w.lists, w.list_off, w.seg_off, (int)z.nkb, w.pdk, w.pdv, (uint16_t*)dk,
+                     (uint16_t*)dv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_kv_reduce_kernel<D>), dim3((unsigned)z.nkb), dim3(256), 0, s, g, w.seg_off, w.pdk, w.pdv,
                      (uint16_t*)dk, (uint16_t*)dv);
