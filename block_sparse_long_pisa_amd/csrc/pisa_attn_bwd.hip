@@ -5,7 +5,8 @@
 //
 // For query row i with attended keys A(i), logits s = scale q_i.k_t, weights
 // p = exp(s - lse_i) (lse from the forward), and dO_i the output gradient:
-//   D_i   = dO_i . O_i                          (bwd_rowdot_kernel)
+//   D_i   = dO_i . O_i                          (bwd_dq_kernel's prologue, which
+//                                               also writes it for the key-centric pass)
 //   dP_it = dO_i . v_t,  dS_it = p_it (dP_it - D_i)
 //   dQ_i  = scale sum_t dS_it k_t               (bwd_dq_kernel: query-centric, the
 //                                               forward's walk and tiles)
@@ -29,39 +30,6 @@ constexpr int kBwdSeg = 64;  // list entries (query blocks) per key-centric segm
 constexpr int kListThreads = 256;
 
 enum : int { kFull = 0, kSinkPart = 1, kLocal = 2 };
-
-// ---------------------------------------------------------------------------
-// D_i = dO_i . O_i, 16 lanes per row; beside it lse_i in log2 units, so that the
-// key-centric pass takes p = exp2(s c - lse2) with one fused multiply-add
-
-template <int D>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const uint16_t* __restrict__ dout,
-                                                         const uint16_t* __restrict__ out, const float* __restrict__ lse,
-                                                         float* __restrict__ rowdot, float* __restrict__ lse2,
-                                                         int64_t rows) {
-  constexpr int PER = D / 16;  // bf16 per lane
-  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  const int64_t rr = r < rows ? r : rows - 1;
-  float s = 0.f;
-  if constexpr (PER == 8) {
-    const uint4 a = *reinterpret_cast<const uint4*>(dout + rr * D + sub * 8);
-    const uint4 o = *reinterpret_cast<const uint4*>(out + rr * D + sub * 8);
-    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, ov[4] = {o.x, o.y, o.z, o.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s += bf16lo(av[e]) * bf16lo(ov[e]) + bf16hi(av[e]) * bf16hi(ov[e]);
-  } else {
-    const uint2 a = *reinterpret_cast<const uint2*>(dout + rr * D + sub * 4);
-    const uint2 o = *reinterpret_cast<const uint2*>(out + rr * D + sub * 4);
-    s = bf16lo(a.x) * bf16lo(o.x) + bf16hi(a.x) * bf16hi(o.x) + bf16lo(a.y) * bf16lo(o.y) + bf16hi(a.y) * bf16hi(o.y);
-  }
-#pragma unroll
-  for (int sh = 1; sh < 16; sh <<= 1) s += __shfl_xor(s, sh);
-  if (sub == 0 && r < rows) {
-    rowdot[r] = s;
-    lse2[r] = lse[r] * kLog2e;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dQ: query-centric. A workgroup serves NW waves x 32 query rows of one
@@ -232,8 +200,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(Geo g, const uint16_t* 
                                                          const int32_t* __restrict__ idx,
                                                          const int32_t* __restrict__ cnt,
                                                          const uint16_t* __restrict__ dout,
-                                                         const float* __restrict__ lse,
-                                                         const float* __restrict__ rowdot, uint16_t* __restrict__ dq,
+                                                         const uint16_t* __restrict__ out,
+                                                         const float* __restrict__ lse, float* __restrict__ rowdot,
+                                                         float* __restrict__ lse2, uint16_t* __restrict__ dq,
                                                          int parts) {
   constexpr int NT = NW * 64;
   constexpr int NDS = D / 16, NDB = D / 32;
@@ -279,8 +248,25 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(Geo g, const uint16_t* 
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) st.acc[db][i] = 0.f;
+  // D_i = dO_i . O_i: this lane's half of the row, then the other half from
+  // lane ^ 32. Each valid row belongs to one wave of one workgroup, which also
+  // writes D_i and lse_i in log2 units for the key-centric pass.
+  float rd = 0.f;
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) {
+    const uint4 uo = qvalid ? *reinterpret_cast<const uint4*>(out + row * D + ds * 16 + hi * 8) : make_uint4(0, 0, 0, 0);
+    const uint4 ud = __builtin_bit_cast(uint4, st.df[ds]);
+    const uint32_t av[4] = {ud.x, ud.y, ud.z, ud.w}, ov[4] = {uo.x, uo.y, uo.z, uo.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rd += bf16lo(av[e]) * bf16lo(ov[e]) + bf16hi(av[e]) * bf16hi(ov[e]);
+  }
+  rd += __shfl_xor(rd, 32);
   st.lse2 = qvalid ? lse[row] * kLog2e : __builtin_inff();
-  st.rd = qvalid ? rowdot[row] : 0.f;
+  st.rd = rd;
+  if (qvalid && hi == 0) {
+    rowdot[row] = rd;
+    lse2[row] = st.lse2;
+  }
   st.init_offsets(lane);
   const float c = g.scale * kLog2e;
   const int wg_qmax = qb * BS + (((part + 1) * NW - 1) / g.G) * 32 + 31;
@@ -826,21 +812,18 @@ hipError_t launch_bwd_t(const Geo& g, const void* q, const void* k, const void* 
   BwdWs w = carve_bwd(g, wsb);
   const uint16_t *qt = (const uint16_t*)q, *kt = (const uint16_t*)k, *vt = (const uint16_t*)v;
   const uint16_t* dot = (const uint16_t*)dout;
-  const int64_t rows = (int64_t)g.B * g.Hq * g.N;
-  hipLaunchKernelGGL((bwd_rowdot_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, dot,
-                     (const uint16_t*)out, lse, w.rowdot, w.lse2, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const uint16_t* ot = (const uint16_t*)out;
+  hipError_t e;
   // dQ: the forward's workgroup shape (8, 4, 2 or 1 waves per part)
   const int waves = g.G * BS / 32;
   const int nw = waves % 8 == 0 ? 8 : waves % 4 == 0 ? 4 : waves % 2 == 0 ? 2 : 1;
   const int parts = waves / nw;
   const unsigned grid = (unsigned)((int64_t)g.nb * g.B * g.Hkv * parts);
   switch (nw) {
-    case 8: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 8>), dim3(grid), dim3(512), 0, s, g, qt, kt, vt, idx, cnt, dot, lse, w.rowdot, (uint16_t*)dq, parts); break;
-    case 4: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 4>), dim3(grid), dim3(256), 0, s, g, qt, kt, vt, idx, cnt, dot, lse, w.rowdot, (uint16_t*)dq, parts); break;
-    case 2: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 2>), dim3(grid), dim3(128), 0, s, g, qt, kt, vt, idx, cnt, dot, lse, w.rowdot, (uint16_t*)dq, parts); break;
-    default: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 1>), dim3(grid), dim3(64), 0, s, g, qt, kt, vt, idx, cnt, dot, lse, w.rowdot, (uint16_t*)dq, parts); break;
+    case 8: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 8>), dim3(grid), dim3(512), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
+    case 4: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 4>), dim3(grid), dim3(256), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
+    case 2: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 2>), dim3(grid), dim3(128), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
+    default: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 1>), dim3(grid), dim3(64), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(bwd_list_kernel, dim3((unsigned)z.nkb), dim3(kListThreads), 0, s, g, idx, cnt, w.counts,
