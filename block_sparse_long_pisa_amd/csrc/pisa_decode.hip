@@ -22,7 +22,7 @@ namespace pisa {
 namespace {
 
 constexpr int kDecThreads = 256;
-constexpr int kTilesPerSplit = 4;
+constexpr int kTilesPerSplit = 6;
 constexpr int kMaxGroup = 8;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
