@@ -163,22 +163,28 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
   const T* kb = k + (int64_t)slab * g.N * D;
   float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
   int a = len0 / g.bs, z = (len1 - 1) / g.bs;  // affected nodes of the level being built
-  for (int j = a + wave; j <= z; j += kPoolThreads / 64) {
+  // each affected leaf with all waves: wave w reads rows r0 + RPI (w + NWV i) + rsub,
+  // the waves' column sums are joined in LDS (the fp64 sum of a block's rows is
+  // exact, so it does not depend on the order of the additions)
+  constexpr int NWV = kPoolThreads / 64;
+  __shared__ typename PO::Acc part[NWV][D];
+  for (int j = a; j <= z; ++j) {
     const int r0 = j * g.bs;
     const int r1 = min(len1, r0 + g.bs);
     typename PO::Acc acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = PO::init();
-    for (int r = r0 + rsub; r < r1; r += RPI * kUnroll) {
+    for (int r = r0 + wave * RPI + rsub; r < r1; r += RPI * NWV * kUnroll) {
       uint4 raw[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) raw[u] = Wide<T>::raw(kb + (int64_t)min(r + u * RPI, r1 - 1) * D + col);
+      for (int u = 0; u < kUnroll; ++u)
+        raw[u] = Wide<T>::raw(kb + (int64_t)min(r + u * RPI * NWV, r1 - 1) * D + col);
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         float x[VEC];
         Wide<T>::widen(raw[u], x);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = PO::add_row(acc[e], x[e], r + u * RPI < r1);
+        for (int e = 0; e < VEC; ++e) acc[e] = PO::add_row(acc[e], x[e], r + u * RPI * NWV < r1);
       }
     }
 #pragma unroll
@@ -187,10 +193,17 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
       for (int e = 0; e < VEC; ++e) acc[e] = PO::join(acc[e], __shfl_xor(acc[e], sh));
     if (rsub == 0) {
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) pb[(int64_t)j * D + col + e] = PO::fin(acc[e], r1 - r0);
+      for (int e = 0; e < VEC; ++e) part[wave][col + e] = acc[e];
     }
+    __syncthreads();
+    for (int c = threadIdx.x; c < D; c += kPoolThreads) {
+      typename PO::Acc sum = part[0][c];
+#pragma unroll
+      for (int w = 1; w < NWV; ++w) sum = PO::join(sum, part[w][c]);
+      pb[(int64_t)j * D + c] = PO::fin(sum, r1 - r0);
+    }
+    __syncthreads();
   }
-  __syncthreads();
   int present = z + 1;  // nodes of the level below that hold tokens before len1
   for (int l = 1; l < g.L; ++l) {
     const int na = a / g.f, nz = z / g.f;
