@@ -164,8 +164,10 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
   float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
   int a = len0 / g.bs, z = (len1 - 1) / g.bs;  // affected nodes of the level being built
   // each affected leaf with all waves: wave w reads rows r0 + RPI (w + NWV i) + rsub,
-  // the waves' column sums are joined in LDS (the fp64 sum of a block's rows is
-  // exact, so it does not depend on the order of the additions)
+  // and the waves' column sums are joined in LDS. The fp64 sum of at most 128
+  // rows is exact, whatever the order of the additions, when a column's values
+  // span at most 38 binades (bf16 keys) or 22 (fp32 keys); only beyond that can
+  // the order move the summary by one unit in its last place.
   constexpr int NWV = kPoolThreads / 64;
   __shared__ typename PO::Acc part[NWV][D];
   for (int j = a; j <= z; ++j) {
