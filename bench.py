@@ -299,7 +299,7 @@ def run_prefill(args, dev):
     import block_sparse_long_pisa_amd as pisa
     import gen
 
-    cfg = gen.config(3)
+    cfg = gen.workload(3)
     p = cfg["problem"]
     cp = pisa.problem(p.batch, p.heads_q, p.heads_kv, p.seq_len, p.head_dim, p.block_size, p.fanout, p.levels,
                       p.top_k, p.sink_len, p.dtype)
@@ -522,7 +522,7 @@ def run_decode(args, dev):
     import block_sparse_long_pisa_amd as pisa
     import gen
 
-    dcfg = gen.config(4)
+    dcfg = gen.workload(4)
     dp = dcfg["problem"]
     dcp = pisa.problem(dp.batch, dp.heads_q, dp.heads_kv, dp.seq_len, dp.head_dim, dp.block_size, dp.fanout,
                        dp.levels, dp.top_k, dp.sink_len, dp.dtype)
@@ -644,7 +644,7 @@ def main(argv=None):
                     help="also run one plain 1 GiB device copy (counter calibration for rocprofv3 --pmc runs)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no multi-GPU path", flush=True)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library runs on one GPU; run with --gpus 1", flush=True)
         return 2
 
     import numpy as np

@@ -37,7 +37,7 @@ import numpy as np
 
 __all__ = [
     "Problem",
-    "CONFIGS",
+    "WORKLOADS",
     "config",
     "round_to_bf16",
     "bf16_bits",
@@ -88,7 +88,7 @@ class Problem:
 
 
 # The five workloads: shapes, seeds and planting schemes.
-CONFIGS: Dict[int, dict] = {
+WORKLOADS: Dict[int, dict] = {
     1: dict(
         name="tiny fp32 causal single head, N=1024",
         problem=Problem(1, 1, 1, 1024, 64, 64, 4, 2, 4, 64, "f32"),
@@ -127,8 +127,8 @@ CONFIGS: Dict[int, dict] = {
 }
 
 
-def config(i: int) -> dict:
-    c = dict(CONFIGS[i])
+def workload(i: int) -> dict:
+    c = dict(WORKLOADS[i])
     if c["value_scale"] is None:
         c["value_scale"] = 1.0 / math.sqrt(c["problem"].head_dim)
     return c

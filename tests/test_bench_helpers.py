@@ -34,7 +34,7 @@ def test_append_bytes_single_token_by_hand():
     # one token at position 1000 (block 7 of 128-token blocks, fanout 8, 4 levels):
     # the leaf re-reads rows 896..1000; level 1 node 0 reads its 8 present children,
     # level 2 node 0 reads its 1 present child, level 3 node 0 its 1
-    p = gen.config(4)["problem"]
+    p = gen.workload(4)["problem"]
     rows = 1001 - 7 * 128
     written = 4  # one node per level
     read = 8 + 1 + 1

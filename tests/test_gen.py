@@ -17,7 +17,7 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_host_inputs_are_deterministic_and_sliceable():
-    c = gen.config(2)
+    c = gen.workload(2)
     p = c["problem"].replace(heads_q=3, heads_kv=3, seq_len=1024)
     a = gen.host_inputs(p, c["seed"], c["value_scale"], c["plant"])
     b = gen.host_inputs(p, c["seed"], c["value_scale"], c["plant"])
@@ -31,7 +31,7 @@ def test_host_inputs_are_deterministic_and_sliceable():
 
 
 def test_planting_writes_the_query_block_mean_plus_small_noise():
-    c = gen.config(3)
+    c = gen.workload(3)
     p = c["problem"].replace(seq_len=8192)
     q, k, v, man = gen.host_inputs(p, c["seed"], c["value_scale"], c["plant"])
     assert len(man["needles"]) == 16 * p.heads_kv

@@ -34,14 +34,14 @@ def _sample_units(p, man, n_random=12, seed=0):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg_id", [1, 2, 3, 5])
-def test_full_prefill(cfg_id):
+@pytest.mark.parametrize("workload_id", [1, 2, 3, 5])
+def test_full_prefill(workload_id):
     import block_sparse_long_pisa_amd as pisa
 
-    c = gen.config(cfg_id)
+    c = gen.workload(workload_id)
     p = c["problem"]
-    log(f"config {cfg_id}: {c['name']}")
-    if cfg_id == 1:
+    log(f"workload {workload_id}: {c['name']}")
+    if workload_id == 1:
         qh, kh, vh, man = gen.host_inputs(p, c["seed"], c["value_scale"], c["plant"])
         q, k, v = to_dev(qh, p.dtype), to_dev(kh, p.dtype), to_dev(vh, p.dtype)
     else:
@@ -53,7 +53,7 @@ def test_full_prefill(cfg_id):
     g_levels = split_levels(to_host(pyr), offs)
     gi, gc = to_host(idx), to_host(cnt)
     del pyr
-    if cfg_id != 1:
+    if workload_id != 1:
         qh, kh, vh = to_host(q), to_host(k), to_host(v)
     log("  GPU done; oracle pyramid")
     o_levels = oracle.build_pyramid(kh, p.block_size, p.fanout, p.levels)
@@ -76,7 +76,7 @@ def test_full_prefill(cfg_id):
     log(f"  {oc.size} selections bit-exact; smallest relative boundary margin "
         f"{min(rel) if rel else float('nan'):.2e}; planted blocks dropped by coarse levels: {dropped}; "
         "oracle attention on sampled blocks")
-    units = _sample_units(p, man) if cfg_id != 1 else None
+    units = _sample_units(p, man) if workload_id != 1 else None
     o, ol = oracle.attend(qh, kh, vh, oi, oc, p.sink_len, p.block_size, p.scale, blocks=units)
     err = assert_outputs_close(p, to_host(out), o, to_host(lse), ol)
     found = sum(1 for n in man["needles"] if n["survived"] and n["target"] in oi[n["b"], n["g"], n["qb"]].tolist())
@@ -87,7 +87,7 @@ def test_full_prefill(cfg_id):
 def test_full_decode():
     import block_sparse_long_pisa_amd as pisa
 
-    c = gen.config(4)
+    c = gen.workload(4)
     p = c["problem"]
     cache_len = p.seq_len
     log(f"config 4: {c['name']}")

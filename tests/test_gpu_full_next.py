@@ -38,7 +38,7 @@ def _close(name, got, want):
 def test_full_backward_128k_gqa():
     import block_sparse_long_pisa_amd as pisa
 
-    c = gen.config(3)
+    c = gen.workload(3)
     p = c["problem"]
     log(f"backward at full size: {c['name']}")
     q, k, v, man = gen.device_inputs(p, c["seed"], c["value_scale"], c["plant"], device="cuda")
@@ -83,7 +83,7 @@ def test_full_backward_128k_gqa():
 def test_full_variants_128k_gqa(causal, pool):
     import block_sparse_long_pisa_amd as pisa
 
-    c = gen.config(3)
+    c = gen.workload(3)
     p = c["problem"].replace(causal=causal, pool=pool)
     log(f"variant causal={causal} pool={pool} at full size: {c['name']}")
     q, k, v, man = gen.device_inputs(p, c["seed"], c["value_scale"], c["plant"], device="cuda")
@@ -109,7 +109,7 @@ def test_full_variants_128k_gqa(causal, pool):
 def test_full_serving_64x128k_ragged():
     import block_sparse_long_pisa_amd as pisa
 
-    c = gen.config(4)
+    c = gen.workload(4)
     p = c["problem"]
     log(f"serving at full size: {c['name']}, ragged lengths")
     qd, kc, vc, _ = gen.device_decode_inputs(p, c["seed"], c["value_scale"], p.seq_len, device="cuda")

@@ -70,13 +70,13 @@ def test_fused_without_selection_outputs():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("cfg_id", [2, 3, 5])
-def test_fused_full_size(cfg_id):
+@pytest.mark.parametrize("workload_id", [2, 3, 5])
+def test_fused_full_size(workload_id):
     import block_sparse_long_pisa_amd as pisa
 
-    c = gen.config(cfg_id)
+    c = gen.workload(workload_id)
     p = c["problem"]
-    log(f"fused, config {cfg_id}: {c['name']}")
+    log(f"fused, config {workload_id}: {c['name']}")
     q, k, v, man = gen.device_inputs(p, c["seed"], c["value_scale"], c["plant"], device="cuda")
     cp = cprob(p)
     out, lse, idx, cnt = _both(pisa, cp, q, k, v)

@@ -27,7 +27,7 @@ P = gen.Problem
 # bf16 rounding of the outputs themselves stays inside the 2e-3 bar
 SHARP = (1.0, 1.0, 1.0 / math.sqrt(128))
 SMALL = {
-    "cfg1_fp32": (gen.CONFIGS[1]["problem"], "every_block", 1.0),
+    "tiny_f32_n1024": (gen.WORKLOADS[1]["problem"], "every_block", 1.0),
     "gqa_ragged": (P(2, 8, 2, 4000, 128, 128, 4, 3, 4, 64, "bf16"), ("uniform_pairs", 4), None),
     "mha_bs64_ragged": (P(1, 4, 4, 3000, 128, 64, 8, 2, 6, 64, "bf16"), ("uniform_pairs", 4), None),
     "d64_partial_sink": (P(1, 4, 1, 2065, 64, 32, 4, 3, 3, 40, "bf16"), ("uniform_pairs", 4), None),

@@ -101,7 +101,7 @@ def test_zero_k_is_sink_plus_local_window():
 
 
 def test_outputs_are_convex_combinations_of_attended_values():
-    c = gen.config(1)
+    c = gen.workload(1)
     p = c["problem"]
     q, k, v, _ = gen.host_inputs(p, c["seed"], c["value_scale"], c["plant"])
     pyr = build_pyramid(k, p.block_size, p.fanout, p.levels)

@@ -88,7 +88,7 @@ def test_each_level_is_the_rounded_mean_of_its_children():
 def test_block_sums_are_exact_on_generated_inputs():
     # The fp64 sum of a block's bf16 keys is exact here, so any summation order
     # (CPU or GPU) gives the same fp32 summary: compare with an exactly rounded sum.
-    c = gen.config(2)
+    c = gen.workload(2)
     p = c["problem"].replace(heads_q=2, heads_kv=2, seq_len=4096)
     q, k, v, _ = gen.host_inputs(p, c["seed"], c["value_scale"], c["plant"])
     pyr = build_pyramid(k, p.block_size, p.fanout, p.levels)

@@ -93,7 +93,7 @@ def _random_case(seed, N, d, bs, f, L, Hq=1, Hkv=1):
 def test_config1_shape_descent_is_exhaustive():
     # 16 blocks, fanout 4, 2 levels, K = 4: the top level never holds more than
     # 3 complete nodes, so nothing is pruned and the descent equals brute force.
-    c = gen.config(1)
+    c = gen.workload(1)
     p = c["problem"]
     q, k, v, man = gen.host_inputs(p, c["seed"], c["value_scale"], c["plant"])
     pyr = build_pyramid(k, p.block_size, p.fanout, p.levels)
