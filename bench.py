@@ -292,25 +292,33 @@ def cpu_baseline(p, q, k, v, seed_units=0):
 # ---------------------------------------------------------------------------
 
 
-def run_prefill(args, dev):
+def median_ms(pairs):
+    """Median of event intervals (start, end) in seconds."""
     import numpy as np
+
+    return float(np.median([a.elapsed_time(b) for a, b in pairs])) * 1e-3
+
+
+def prefill_buffers(p, cp, dev):
     import torch
 
     import block_sparse_long_pisa_amd as pisa
-    import gen
 
-    cfg = gen.workload(3)
-    p = cfg["problem"]
-    cp = pisa.problem(p.batch, p.heads_q, p.heads_kv, p.seq_len, p.head_dim, p.block_size, p.fanout, p.levels,
-                      p.top_k, p.sink_len, p.dtype)
-    log(f"generating {cfg['name']} on the GPU")
-    q, k, v, _ = gen.device_inputs(p, cfg["seed"], cfg["value_scale"], cfg["plant"], device=dev)
     nodes = pisa.pyramid_layout(cp)[-1]
     nb = p.n_blocks
     pyr = torch.empty((p.batch, p.heads_kv, nodes, p.head_dim), dtype=torch.float32, device=dev)
     idx = torch.empty((p.batch, p.heads_kv, nb, p.top_k), dtype=torch.int32, device=dev)
     cnt = torch.empty((p.batch, p.heads_kv, nb), dtype=torch.int32, device=dev)
-    out = torch.empty_like(q)
+    return nodes, pyr, idx, cnt
+
+
+def time_prefill(p, cp, q, k, v, pyr, idx, cnt, out, steps, warmup):
+    """Wall time per step over `steps` steps (after `warmup`), then the median
+    HIP-event time of each kernel over `steps` more steps. Events are recorded on
+    torch's current stream, the stream the binding launches on."""
+    import torch
+
+    import block_sparse_long_pisa_amd as pisa
 
     def step(ev=None):
         if ev is not None:
@@ -326,30 +334,109 @@ def run_prefill(args, dev):
             ev[3].record()
 
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed / args.steps * 1e3
-    # per-kernel durations with HIP events on the launch stream (torch's current stream)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for e in evs:
         step(e)
     torch.cuda.synchronize()
-    t_pool = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
-    t_sel = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
-    t_att = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e-3
+    t_pool = median_ms([(e[0], e[1]) for e in evs])
+    t_sel = median_ms([(e[1], e[2]) for e in evs])
+    t_att = median_ms([(e[2], e[3]) for e in evs])
+    return elapsed / steps, t_pool, t_sel, t_att
+
+
+def kernel_lines(p, nodes, idx, cnt, t_pool, t_sel, t_att, traffic=True):
     idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
     pairs = attended_pairs(p, idx_h, cnt_h)
     flops = 4.0 * p.head_dim * pairs
     b_pool = pyramid_bytes(p, nodes)
     b_sel = select_bytes(p, nodes)
+    tr = measured_traffic if traffic else (lambda _: None)
+    return flops, pairs, {
+        "pyramid": {"ms": t_pool * 1e3, "bound": "hbm", "bytes": b_pool, "GB/s": b_pool / t_pool / 1e9,
+                    "frac": b_pool / t_pool / HBM_PEAK, "traffic": tr("pyramid")},
+        "select": {"ms": t_sel * 1e3, "bound": "hbm", "bytes": b_sel, "GB/s": b_sel / t_sel / 1e9,
+                   "frac": b_sel / t_sel / HBM_PEAK, "traffic": tr("select")},
+        "attention": {"ms": t_att * 1e3, "bound": "mfma", "flops": flops, "TFLOP/s": flops / t_att / 1e12,
+                      "frac": flops / t_att / BF16_PEAK, "attended_pairs": pairs, "traffic": tr("attention")},
+    }
+
+
+WORKLOAD_TEXT = {
+    2: "PISA prefill, bf16 causal MHA 32 heads, N=32768, d=128, block 64, fanout 8, 3 levels, K=16, 64-token sink, "
+       "1 local block; 8 planted (query block, target) pairs per head",
+    3: "PISA prefill, bf16 causal GQA 32q/8kv heads, N=131072, d=128, block 128, fanout 8, 4 levels, K=32, "
+       "64-token sink, 1 local block; planted needles at 16 depths per KV head",
+    5: "PISA prefill, bf16 causal one GQA group 4q/1kv heads, N=1048576, d=128, block 128, fanout 8, 5 levels, "
+       "K=64, 64-token sink, 1 local block; 32 planted needles at log-uniform distances",
+}
+
+
+def run_other_prefill(wid, args, dev):
+    """One more prefill workload timed like the headline one (its own line under
+    `workloads`, not the headline value)."""
+    import torch
+
+    import block_sparse_long_pisa_amd as pisa
+    import gen
+
+    cfg = gen.workload(wid)
+    p = cfg["problem"]
+    cp = pisa.problem(p.batch, p.heads_q, p.heads_kv, p.seq_len, p.head_dim, p.block_size, p.fanout, p.levels,
+                      p.top_k, p.sink_len, p.dtype)
+    log(f"generating {cfg['name']} on the GPU")
+    q, k, v, _ = gen.device_inputs(p, cfg["seed"], cfg["value_scale"], cfg["plant"], device=dev)
+    nodes, pyr, idx, cnt = prefill_buffers(p, cp, dev)
+    out = torch.empty_like(q)
+    steps = args.workload_steps
+    t_step, t_pool, t_sel, t_att = time_prefill(p, cp, q, k, v, pyr, idx, cnt, out, steps, args.warmup)
+    flops, pairs, kernels = kernel_lines(p, nodes, idx, cnt, t_pool, t_sel, t_att, traffic=False)
+    log(f"workload {wid}: {t_step * 1e3:.3f} ms/step: pyramid {t_pool * 1e3:.3f} ms "
+        f"({kernels['pyramid']['frac'] * 100:.0f}% HBM), select {t_sel * 1e3:.3f} ms "
+        f"({kernels['select']['frac'] * 100:.0f}% HBM), attention {t_att * 1e3:.3f} ms "
+        f"({kernels['attention']['frac'] * 100:.1f}% MFMA)")
+    del q, k, v, out, pyr, idx, cnt
+    torch.cuda.empty_cache()
+    return {
+        "workload": WORKLOAD_TEXT[wid],
+        "seed": cfg["seed"],
+        "steps": steps,
+        "ms_per_step": t_step * 1e3,
+        "tokens_per_s": p.batch * p.seq_len / t_step,
+        "kernel_sum_ms": (t_pool + t_sel + t_att) * 1e3,
+        "tokens_per_s_kernels": p.batch * p.seq_len / (t_pool + t_sel + t_att),
+        "kernels": kernels,
+    }
+
+
+def run_prefill(args, dev):
+    import numpy as np
+    import torch
+
+    import block_sparse_long_pisa_amd as pisa
+    import gen
+
+    cfg = gen.workload(3)
+    p = cfg["problem"]
+    cp = pisa.problem(p.batch, p.heads_q, p.heads_kv, p.seq_len, p.head_dim, p.block_size, p.fanout, p.levels,
+                      p.top_k, p.sink_len, p.dtype)
+    log(f"generating {cfg['name']} on the GPU")
+    q, k, v, _ = gen.device_inputs(p, cfg["seed"], cfg["value_scale"], cfg["plant"], device=dev)
+    nodes, pyr, idx, cnt = prefill_buffers(p, cp, dev)
+    nb = p.n_blocks
+    out = torch.empty_like(q)
+    log(f"warmup {args.warmup}, timing {args.steps} steps")
+    t_step, t_pool, t_sel, t_att = time_prefill(p, cp, q, k, v, pyr, idx, cnt, out, args.steps, args.warmup)
+    elapsed = t_step * args.steps
+    ms_per_step = t_step * 1e3
+    flops, pairs, kernels = kernel_lines(p, nodes, idx, cnt, t_pool, t_sel, t_att)
     log(f"prefill {ms_per_step:.3f} ms/step: pyramid {t_pool * 1e3:.3f} ms, select {t_sel * 1e3:.3f} ms, "
         f"attention {t_att * 1e3:.3f} ms ({flops / t_att / 1e12:.1f} TFLOP/s)")
 
@@ -384,14 +471,7 @@ def run_prefill(args, dev):
             "algorithmic_flops_per_launch": flops,
             "avg_launch_ms": t_att * 1e3,
         },
-        "kernels": {
-            "pyramid": {"ms": t_pool * 1e3, "bound": "hbm", "bytes": b_pool, "GB/s": b_pool / t_pool / 1e9,
-                        "frac": b_pool / t_pool / HBM_PEAK, "traffic": measured_traffic("pyramid")},
-            "select": {"ms": t_sel * 1e3, "bound": "hbm", "bytes": b_sel, "GB/s": b_sel / t_sel / 1e9,
-                       "frac": b_sel / t_sel / HBM_PEAK, "traffic": measured_traffic("select")},
-            "attention": {"ms": t_att * 1e3, "bound": "mfma", "flops": flops, "TFLOP/s": flops / t_att / 1e12,
-                          "frac": flops / t_att / BF16_PEAK, "attended_pairs": pairs, "traffic": measured_traffic("attention")},
-        },
+        "kernels": kernels,
     }
 
     if args.fused:
@@ -407,7 +487,7 @@ def run_prefill(args, dev):
             pisa.select_attend(cp, q, k, v, pyr, idx, cnt, out)
             e[1].record()
         torch.cuda.synchronize()
-        t_fu = float(np.mean([e[0].elapsed_time(e[1]) for e in fe])) * 1e-3
+        t_fu = median_ms([(e[0], e[1]) for e in fe])
         log(f"fused select+attend {t_fu * 1e3:.3f} ms, against select + attention {(t_sel + t_att) * 1e3:.3f} ms")
         result["fused"] = {
             "workload": "the same prefill: pisa_select_attend (query mean, descent and attention in one launch) "
@@ -446,8 +526,8 @@ def run_prefill(args, dev):
             for e in ve:
                 vstep(e)
             torch.cuda.synchronize()
-            t_ps = float(np.mean([e[0].elapsed_time(e[1]) for e in ve])) * 1e-3
-            t_at = float(np.mean([e[1].elapsed_time(e[2]) for e in ve])) * 1e-3
+            t_ps = median_ms([(e[0], e[1]) for e in ve])
+            t_at = median_ms([(e[1], e[2]) for e in ve])
             ih, ch = idx.cpu().numpy(), cnt.cpu().numpy()
             vpairs = attended_pairs(p, ih, ch) if causal else attended_pairs_bidirectional(p, ih, ch)
             vfl = 4.0 * p.head_dim * vpairs
@@ -480,7 +560,7 @@ def run_prefill(args, dev):
             pisa.sparse_attn_bwd(cp, q, k, v, idx, cnt, out, lse, dout, dq, dk, dv, workspace=bws)
             e[1].record()
         torch.cuda.synchronize()
-        t_bwd = float(np.mean([e[0].elapsed_time(e[1]) for e in be])) * 1e-3
+        t_bwd = median_ms([(e[0], e[1]) for e in be])
         bflops = 10.0 * p.head_dim * pairs  # S, dP, dV, dK, dQ products over the attended pairs
         log(f"backward {t_bwd * 1e3:.3f} ms ({bflops / t_bwd / 1e12:.1f} TFLOP/s)")
         result["backward"] = {
@@ -593,8 +673,8 @@ def run_decode(args, dev):
         serve(args.warmup + i, evs[i])
     torch.cuda.synchronize()
     t_srv = (time.perf_counter() - t0) / args.decode_steps
-    t_app = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e-3
-    t_rdec = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e-3
+    t_app = median_ms([(e[0], e[1]) for e in evs])
+    t_rdec = median_ms([(e[1], e[2]) for e in evs])
     last = args.warmup + args.decode_steps - 1
     rb = decode_bytes(dp, lens_h[last + 1].tolist(), dcnt.cpu().numpy())
     ab = append_bytes(dp, lens_h[last].tolist(), lens_h[last + 1].tolist())
@@ -622,8 +702,12 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="run one workload only (profiling); the JSON line then lacks the other")
+    ap.add_argument("--only", choices=["prefill", "decode", "w2", "w5"], default=None,
+                    help="run one workload only (profiling); the JSON line then lacks the others")
+    ap.add_argument("--workloads", dest="workloads", action="store_true", default=True,
+                    help="also time the 32K MHA and the 1M single-group prefill workloads (default)")
+    ap.add_argument("--no-workloads", dest="workloads", action="store_false")
+    ap.add_argument("--workload-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", dest="backward", action="store_true", default=True,
                     help="also time the backward pass on the prefill workload (default)")
@@ -657,10 +741,16 @@ def main(argv=None):
     torch.cuda.set_device(dev)
     if args.only == "decode":
         result = {"metric": "decode µs/step (profiling run)", "decode": run_decode(args, dev)}
+    elif args.only in ("w2", "w5"):
+        wid = int(args.only[1])
+        result = {"metric": f"prefill workload {wid} (profiling run)", "workload": run_other_prefill(wid, args, dev)}
     else:
         result = run_prefill(args, dev)
-        if not args.no_decode and args.only is None:
-            result["decode"] = run_decode(args, dev)
+        if args.only is None:
+            if args.workloads:
+                result["workloads"] = {f"w{w}": run_other_prefill(w, args, dev) for w in (2, 5)}
+            if not args.no_decode:
+                result["decode"] = run_decode(args, dev)
     print(json.dumps(result), flush=True)
     return 0
 

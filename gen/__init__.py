@@ -38,7 +38,7 @@ import numpy as np
 __all__ = [
     "Problem",
     "WORKLOADS",
-    "config",
+    "workload",
     "round_to_bf16",
     "bf16_bits",
     "host_inputs",

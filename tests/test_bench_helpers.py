@@ -56,3 +56,15 @@ def test_bidirectional_pairs_count_every_attended_key_once():
             sel = idx[0, g, qb, :cnt[0, g, qb]].tolist()
             brute += len(oracle.attended_keys(i, sel, p.sink_len, p.block_size, causal=False, n=p.seq_len))
     assert bench.attended_pairs_bidirectional(p, idx, cnt) == brute * p.group
+
+
+def test_median_ms_takes_the_median_of_event_intervals():
+    class Ev:
+        def __init__(self, t):
+            self.t = t
+
+        def elapsed_time(self, other):
+            return other.t - self.t
+
+    pairs = [(Ev(0.0), Ev(d)) for d in (5.0, 1.0, 100.0, 2.0, 3.0)]
+    assert bench.median_ms(pairs) == 3.0e-3

@@ -44,3 +44,10 @@ def test_planting_writes_the_query_block_mean_plus_small_noise():
         target = q[b, g * G:(g + 1) * G, qb * bs:(qb + 1) * bs].astype(np.float64).mean(axis=(0, 1))
         dev = k[b, g, t * bs:(t + 1) * bs].astype(np.float64) - target
         assert abs(dev.std() - 0.1) < 0.01 and abs(dev.mean()) < 0.01
+
+
+def test_star_import_names_exist():
+    ns = {}
+    exec("from gen import *", ns)
+    for name in gen.__all__:
+        assert name in ns, name
