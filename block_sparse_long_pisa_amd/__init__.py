@@ -34,6 +34,8 @@ __all__ = [
     "decode_workspace_size",
     "decode_step",
     "decode_step_ragged",
+    "decode_step_ragged_noalloc",
+    "DECODE_SCRATCH_BYTES",
     "pyramid_append",
     "prefill",
 ]
@@ -52,6 +54,7 @@ EXPORTED_SYMBOLS = [
     "pisa_decode_workspace_size",
     "pisa_decode_step",
     "pisa_decode_step_ragged",
+    "pisa_decode_step_ragged_noalloc",
     "pisa_pyramid_append",
     "pisa_status_string",
     "pisa_last_error",
@@ -138,6 +141,7 @@ def load_library():
         "pisa_sparse_attn_bwd": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "pisa_decode_step": [P, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "pisa_decode_step_ragged": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
+        "pisa_decode_step_ragged_noalloc": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "pisa_pyramid_append": [P, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
@@ -401,6 +405,36 @@ def decode_step_ragged(p: Problem, q, k_cache, v_cache, pyramid, cache_lens, out
     _check(lib.pisa_decode_step_ragged(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pyramid),
                                        _ptr(cache_lens), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(cnt_out),
                                        _ptr(workspace), workspace.numel(), _stream(q)), "pisa_decode_step_ragged")
+    return out, lse, idx_out, cnt_out
+
+
+DECODE_SCRATCH_BYTES = 16 << 20  # PISA_DECODE_SCRATCH_BYTES in include/pisa.h
+
+
+def decode_step_ragged_noalloc(p: Problem, q, k_cache, v_cache, pyramid, cache_lens, out, lse=None, idx_out=None,
+                               cnt_out=None):
+    """decode_step_ragged with the library's static per-GPU workspace: nothing is
+    allocated, so every output buffer (out; lse, idx_out, cnt_out if wanted) is
+    the caller's. Calls on one GPU share the workspace: overlapping calls race."""
+    torch = _torch()
+    lib = load_library()
+    dt = _tdtype(p)
+    nodes = pyramid_layout(p)[-1]
+    _expect(q, (p.batch, p.heads_q, p.head_dim), dt, "q")
+    _expect(k_cache, (p.batch, p.heads_kv, p.seq_len, p.head_dim), dt, "k_cache")
+    _expect(v_cache, (p.batch, p.heads_kv, p.seq_len, p.head_dim), dt, "v_cache")
+    _expect(pyramid, (p.batch, p.heads_kv, nodes, p.head_dim), torch.float32, "pyramid")
+    _expect(cache_lens, (p.batch,), torch.int32, "cache_lens")
+    _expect(out, tuple(q.shape), dt, "out")
+    if lse is not None:
+        _expect(lse, (p.batch, p.heads_q), torch.float32, "lse")
+    if idx_out is not None:
+        _expect(idx_out, (p.batch, p.heads_kv, p.top_k), torch.int32, "idx_out")
+    if cnt_out is not None:
+        _expect(cnt_out, (p.batch, p.heads_kv), torch.int32, "cnt_out")
+    _check(lib.pisa_decode_step_ragged_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pyramid),
+                                               _ptr(cache_lens), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(cnt_out),
+                                               _stream(q)), "pisa_decode_step_ragged_noalloc")
     return out, lse, idx_out, cnt_out
 
 

@@ -293,6 +293,29 @@ pisa_status pisa_decode_step_ragged(const pisa_problem* p, const void* q, const 
   return e == hipSuccess ? ok() : hip_fail(e, "pisa_decode_step_ragged launch");
 }
 
+pisa_status pisa_decode_step_ragged_noalloc(const pisa_problem* p, const void* q, const void* k_cache,
+                                            const void* v_cache, const float* pyramid, const int32_t* cache_lens,
+                                            void* out, float* lse, int32_t* idx_out, int32_t* cnt_out,
+                                            hipStream_t stream) {
+  pisa::Geo g;
+  pisa_status s = make_geo(p, &g);
+  if (s != PISA_OK) return s;
+  if (g.B == 0) return ok();
+  if (cache_lens == nullptr) return fail(PISA_ERR_NULL, "cache_lens is NULL");
+  if (((uintptr_t)cache_lens & 3u) != 0) return fail(PISA_ERR_ALIGN, "cache_lens must be 4-byte aligned");
+  const size_t need = pisa::decode_workspace_bytes(g);
+  if (need > pisa::kDecodeScratchBytes)
+    return fail(PISA_ERR_WORKSPACE, "this problem needs a %zu-byte decode workspace; the static one holds %zu bytes",
+                need, pisa::kDecodeScratchBytes);
+  void* ws = nullptr;
+  hipError_t e = pisa::decode_scratch_ptr(&ws);
+  if (e != hipSuccess) return hip_fail(e, "pisa_decode_step_ragged_noalloc scratch lookup");
+  s = check_decode(g, q, k_cache, v_cache, pyramid, out, ws, pisa::kDecodeScratchBytes);
+  if (s != PISA_OK) return s;
+  e = pisa::launch_decode(g, q, k_cache, v_cache, pyramid, cache_lens, 0, out, lse, idx_out, cnt_out, ws, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "pisa_decode_step_ragged_noalloc launch");
+}
+
 pisa_status pisa_pyramid_append(const pisa_problem* p, const void* k_cache, float* pyramid, const int32_t* old_lens,
                                 const int32_t* new_lens, hipStream_t stream) {
   pisa::Geo g;

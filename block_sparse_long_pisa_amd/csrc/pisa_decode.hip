@@ -15,11 +15,21 @@
 //                  writes (max, sum, unnormalised output) per query head;
 //   decode_merge   one workgroup per (batch, query head): merges the splits.
 // The step is bound by HBM: it reads each attended K/V row exactly once.
+#include <mutex>
+
 #include "pisa_internal.h"
 #include "pisa_select_common.h"
 
 namespace pisa {
 namespace {
+
+// Workspace of the allocation-free decode entry point: one copy per GPU, held
+// from the library's first use on that GPU until the process ends. Host code
+// never passes this name to a kernel: on the host it is only a stand-in for the
+// symbol, and the device address comes from hipGetSymbolAddress (scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
 
 constexpr int kDecThreads = 256;
 constexpr int kTilesPerSplit = 6;
@@ -378,6 +388,27 @@ DecodeWs carve(const Geo& g, void* base, int splits) {
 }
 
 }  // namespace
+
+// Device address of this GPU's scratch array, looked up once per device (with
+// that device current) and kept.
+hipError_t decode_scratch_ptr(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 // Worst-case block count of the walk: sink blocks, selected blocks, local block.
 int decode_splits(const Geo& g, int /*cache_len*/) {

@@ -109,6 +109,9 @@ hipError_t launch_attn_bwd(const Geo& g, const void* q, const void* k, const voi
 // decode: selection of one token per (batch, kv head), split attention, merge
 int decode_splits(const Geo& g, int cache_len);
 size_t decode_workspace_bytes(const Geo& g);
+// the allocation-free decode's workspace: a static device array per GPU
+constexpr size_t kDecodeScratchBytes = (size_t)PISA_DECODE_SCRATCH_BYTES;
+hipError_t decode_scratch_ptr(void** ptr);
 // lens: per-sequence cache lengths on the device, or nullptr for cache_len everywhere
 hipError_t launch_decode(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr,
                          const int32_t* lens, int cache_len, void* out, float* lse, int32_t* idx, int32_t* cnt, void* ws,

@@ -23,7 +23,8 @@
  * Conventions shared by every call:
  *   - All tensors are caller-owned device memory, contiguous, row-major, 16-byte
  *     aligned. The library never allocates or frees device memory and keeps no
- *     mutable global state; calls are thread-safe.
+ *     mutable global state, except the static per-GPU workspace of
+ *     pisa_decode_step_ragged_noalloc; every other call is thread-safe.
  *   - Q, K, V, O use the layout [batch, heads, tokens, head_dim] in the problem's
  *     dtype (fp32 or bf16). The pyramid is fp32 [batch, heads_kv, nodes, head_dim]
  *     with the levels stored one after another, finest first
@@ -218,6 +219,27 @@ pisa_status pisa_decode_step_ragged(const pisa_problem* p, const void* q, const 
                                     const float* pyramid, const int32_t* cache_lens, void* out, float* lse,
                                     int32_t* idx_out, int32_t* cnt_out, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
+
+/* Largest decode workspace the allocation-free entry point can serve: 16 MiB
+ * (workload of 64 sequences x 8 KV heads x 4 query heads per KV head, d = 128,
+ * K = 32 needs about 6.5 MiB). */
+#define PISA_DECODE_SCRATCH_BYTES (16u << 20)
+
+/* pisa_decode_step_ragged for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and results (bit for bit) as pisa_decode_step_ragged,
+ * without the workspace pair: the workspace is a static device array of
+ * PISA_DECODE_SCRATCH_BYTES owned by the library, one per GPU, held from the
+ * first call on that GPU until the process ends. The call allocates nothing.
+ *   Returns PISA_ERR_WORKSPACE (nothing launched) when the problem needs more
+ *   than PISA_DECODE_SCRATCH_BYTES (pisa_decode_workspace_size tells the need).
+ *   Every call on one GPU shares that GPU's array and overwrites it; nothing in
+ *   it has to start at zero. Calls that overlap on one GPU (other streams, other
+ *   host threads) race on it and must be serialised by the caller. */
+pisa_status pisa_decode_step_ragged_noalloc(const pisa_problem* p, const void* q, const void* k_cache,
+                                            const void* v_cache, const float* pyramid, const int32_t* cache_lens,
+                                            void* out, float* lse, int32_t* idx_out, int32_t* cnt_out,
+                                            hipStream_t stream);
 
 /* Bring the pyramid up to date after tokens were appended to the key cache
  * ("Le pooling comme première réduction": a node summarises its keys, so only
