@@ -113,7 +113,9 @@ def problem(batch, heads_q, heads_kv, seq_len, head_dim, block_size, fanout, lev
 
 
 def library_path() -> str:
-    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpisa.so")
+    """The in-tree libpisa.so, or the file PISA_LIBRARY names (e.g. the host-sanitised build)."""
+    return os.environ.get("PISA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                          "libpisa.so")
 
 
 _lib = None

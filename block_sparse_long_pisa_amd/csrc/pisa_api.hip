@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <string>
 
@@ -136,7 +137,11 @@ hipError_t device_cus(int* cus) {
 extern "C" {
 
 const char* pisa_status_string(pisa_status s) {
-  switch (s) {
+  // a C caller may pass any int: read its bits as one, since loading an enum
+  // object that holds a value outside the enumeration is undefined in C++
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case PISA_OK: return "ok";
     case PISA_ERR_NULL: return "null pointer";
     case PISA_ERR_SHAPE: return "invalid shape";

@@ -163,46 +163,61 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
   const T* kb = k + (int64_t)slab * g.N * D;
   float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
   int a = len0 / g.bs, z = (len1 - 1) / g.bs;  // affected nodes of the level being built
-  // each affected leaf with all waves: wave w reads rows r0 + RPI (w + NWV i) + rsub,
-  // and the waves' column sums are joined in LDS. The fp64 sum of at most 128
-  // rows is exact, whatever the order of the additions, when a column's values
-  // span at most 38 binades (bf16 keys) or 22 (fp32 keys); only beyond that can
-  // the order move the summary by one unit in its last place.
-  constexpr int NWV = kPoolThreads / 64;
-  __shared__ typename PO::Acc part[NWV][D];
+  // Each affected leaf: all waves copy its rows into LDS, then the first wave sums
+  // them exactly as pool_leaf_kernel sums a block -- lane slot rsub adds rows
+  // r0 + rsub, r0 + rsub + RPI, ... in ascending order, in rounds of kUnroll rows,
+  // the rows of a last partial round past r1 adding +0.0; then the slots fold by
+  // xor over the lane bits -- so the summary equals the build's bit for bit.
+  __shared__ uint4 rows[128 * D / Wide<T>::kVec];  // up to 128 rows of this lane layout's 16-byte units
   for (int j = a; j <= z; ++j) {
     const int r0 = j * g.bs;
     const int r1 = min(len1, r0 + g.bs);
-    typename PO::Acc acc[VEC];
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = PO::init();
-    for (int r = r0 + wave * RPI + rsub; r < r1; r += RPI * NWV * kUnroll) {
-      uint4 raw[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-        raw[u] = Wide<T>::raw(kb + (int64_t)min(r + u * RPI * NWV, r1 - 1) * D + col);
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        float x[VEC];
-        Wide<T>::widen(raw[u], x);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = PO::add_row(acc[e], x[e], r + u * RPI * NWV < r1);
-      }
-    }
-#pragma unroll
-    for (int sh = LPR; sh < 64; sh <<= 1)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = PO::join(acc[e], __shfl_xor(acc[e], sh));
-    if (rsub == 0) {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) part[wave][col + e] = acc[e];
-    }
+    const int units = (r1 - r0) * LPR;  // 16-byte units of the leaf's rows present
+    const T* src = kb + (int64_t)r0 * D;
+    for (int e = threadIdx.x; e < units; e += kPoolThreads)
+      rows[e] = Wide<T>::raw(src + (int64_t)(e / LPR) * D + (e % LPR) * VEC);
     __syncthreads();
-    for (int c = threadIdx.x; c < D; c += kPoolThreads) {
-      typename PO::Acc sum = part[0][c];
+    if (wave == 0) {
+      typename PO::Acc acc[VEC];
 #pragma unroll
-      for (int w = 1; w < NWV; ++w) sum = PO::join(sum, part[w][c]);
-      pb[(int64_t)j * D + c] = PO::fin(sum, r1 - r0);
+      for (int e = 0; e < VEC; ++e) acc[e] = PO::init();
+      const int nfull = (r1 - r0) / (RPI * kUnroll);
+      int rr = rsub;  // row within the leaf
+      for (int it = 0; it < nfull; ++it) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u, rr += RPI) {
+          float x[VEC];
+          Wide<T>::widen(rows[rr * LPR + col / VEC], x);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[e] = PO::add(acc[e], x[e]);
+        }
+      }
+      if (nfull * RPI * kUnroll < r1 - r0) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u, rr += RPI) {
+          // rows past the leaf add +0.0 to the sum (the maximum ignores them)
+          uint4 raw = rr < r1 - r0 ? rows[rr * LPR + col / VEC] : make_uint4(0u, 0u, 0u, 0u);
+          if constexpr (MX)
+            if (rr >= r1 - r0) raw = rows[(r1 - r0 - 1) * LPR + col / VEC];
+          float x[VEC];
+          Wide<T>::widen(raw, x);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[e] = PO::add(acc[e], x[e]);
+        }
+      }
+#pragma unroll
+      for (int sh = LPR; sh < 64; sh <<= 1)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] = PO::join(acc[e], __shfl_xor(acc[e], sh));
+      if (rsub == 0) {
+        float outv[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) outv[e] = PO::fin(acc[e], r1 - r0);
+        float* dst = pb + (int64_t)j * D + col;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 4)
+          *reinterpret_cast<float4*>(dst + e) = make_float4(outv[e], outv[e + 1], outv[e + 2], outv[e + 3]);
+      }
     }
     __syncthreads();
   }

@@ -155,8 +155,13 @@ pisa_status pisa_sparse_attn_fwd(const pisa_problem* p, const void* q, const voi
  * Each workgroup of the attention grid computes its query block's mean and
  * descends the pyramid itself before attending, so no selection passes through
  * HBM. Implemented for bf16 causal problems; other problems return
- * PISA_ERR_UNSUPPORTED. The selection equals pisa_select_topk's bit for bit and,
- * given it, out and lse equal pisa_sparse_attn_fwd's bit for bit. */
+ * PISA_ERR_UNSUPPORTED. The query mean adds the block's rows in another order than
+ * pisa_select_topk, so the selection equals pisa_select_topk's bit for bit when
+ * each column's fp64 sum is exact -- always when a column of the query block's
+ * values spans at most 35 binades -- and, given the selection, out and lse equal
+ * pisa_sparse_attn_fwd's bit for bit. The two-launch path (pisa_select_topk, then
+ * pisa_sparse_attn_fwd) is the faster one on MI355X; this entry point is kept for
+ * callers that must not hold the selection in memory. */
 pisa_status pisa_select_attend(const pisa_problem* p, const void* q, const void* k, const void* v,
                                const float* pyramid, int32_t* idx, int32_t* cnt, void* out, float* lse,
                                hipStream_t stream);

@@ -112,3 +112,48 @@ def test_full_decode():
         planted = [n for n in man["needles"] if n["b"] == b]
         found = sum(1 for n in planted if n["target"] in oi[0, n["g"]].tolist())
         log(f"    max abs err {err:.2e}; planted blocks selected {found}/{len(planted)}")
+
+
+@pytest.mark.timeout(300)
+def test_million_token_prefill_holds_no_score_matrix():
+    """No N x N score matrix, nor any buffer beyond the call's own: at 1M tokens
+    (one GQA group, 4 query heads), the prefill's peak device memory is the
+    inputs, the outputs (out, lse), the pyramid, the selection (idx, cnt) and
+    nothing else -- torch's allocator sees only those, and the driver's free
+    memory drops by no more than what torch itself reserved (the library
+    allocates nothing of its own)."""
+    import block_sparse_long_pisa_amd as pisa
+
+    c = gen.workload(5)
+    p = c["problem"]
+    cp = cprob(p)
+    q, k, v, _ = gen.device_inputs(p, c["seed"], c["value_scale"], c["plant"], device="cuda")
+    # load the library's code objects with one small call first
+    small = gen.Problem(1, 4, 1, 4096, 128, 128, 8, 3, 8, 64, "bf16")
+    qs, ks, vs, _ = gen.device_inputs(small, 5, c["value_scale"], None, device="cuda")
+    pisa.prefill(cprob(small), qs, ks, vs, want_lse=True)
+    del qs, ks, vs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    reserved0 = torch.cuda.memory_reserved()
+    free0 = torch.cuda.mem_get_info()[0]
+    out, lse, idx, cnt, pyr = pisa.prefill(cp, q, k, v, want_lse=True)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    nodes = pisa.pyramid_layout(cp)[-1]
+    nb = p.n_blocks
+    expected = (q.numel() * 2                                        # out
+                + p.batch * p.heads_q * p.seq_len * 4                # lse
+                + p.batch * p.heads_kv * nodes * p.head_dim * 4      # pyramid
+                + p.batch * p.heads_kv * nb * (p.top_k + 1) * 4)     # idx, cnt
+    allowance = 2 << 20  # allocator rounding of the five buffers
+    log(f"  peak {peak / 2**20:.1f} MiB above the inputs; outputs, pyramid and selection {expected / 2**20:.1f} MiB")
+    assert peak <= expected + allowance
+    drop = free0 - torch.cuda.mem_get_info()[0]
+    grown = torch.cuda.memory_reserved() - reserved0
+    assert drop <= grown + allowance, f"device memory fell by {drop} bytes, torch reserved {grown}"
+    dense = p.batch * p.heads_q * p.seq_len * p.seq_len * 2  # one bf16 score matrix
+    assert peak < dense // 1000
+    del out, lse, idx, cnt, pyr

@@ -250,3 +250,38 @@ def test_append_may_run_beside_the_decode_of_its_step():
         for x, y, z in zip(a[s], b[s], c[s]):
             assert np.array_equal(x, y) and np.array_equal(x, z), f"step {s}"
     log(f"  lengths {lens[0]} -> {lens[-1]}: three orders identical, counts {a[-1][3].reshape(-1).tolist()}")
+
+
+def test_append_matches_the_build_bit_for_bit_on_keys_spanning_many_binades():
+    """fp32 keys whose columns mix values near 1e4, 1 and 1e-12 (over 50 binades):
+    the fp64 column sums of a block are then inexact, so only the same order of
+    additions makes two summaries agree. The append must equal, bit for bit, a
+    fresh build over exactly the appended prefix, and both stay within one fp32
+    unit in the last place of the oracle (whose numpy sums add in another order)."""
+    import block_sparse_long_pisa_amd as pisa
+
+    p = P(3, 2, 2, 1000, 128, 128, 4, 3, 4, 64, "f32")
+    rng = np.random.default_rng(77)
+    k = rng.standard_normal((p.batch, p.heads_kv, p.seq_len, p.head_dim))
+    scale = rng.choice(np.array([1e4, 1.0, 1e-12]), size=k.shape, p=[0.05, 0.45, 0.5])
+    k = (k * scale).astype(np.float32)
+    old, new = [0, 130, 900], [127, 385, 1000]
+    cp = cprob(p)
+    kd = to_dev(k, p.dtype)
+    offs = pisa.pyramid_layout(cp)
+    pyr = pisa.build_pyramid(cp, kd)
+    pisa.pyramid_append(cp, kd, pyr, torch.tensor(old, dtype=torch.int32, device="cuda"),
+                        torch.tensor(new, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    after = split_levels(to_host(pyr), offs)
+    for b in range(p.batch):
+        n = new[b]
+        pb = p.replace(batch=1, seq_len=n)
+        cpb = cprob(pb)
+        fresh = split_levels(to_host(pisa.build_pyramid(cpb, to_dev(k[b:b + 1, :, :n], p.dtype))),
+                             pisa.pyramid_layout(cpb))
+        want = oracle.build_pyramid(k[b:b + 1, :, :n], p.block_size, p.fanout, p.levels)
+        for l in range(p.levels):
+            got = after[l][b:b + 1, :, :fresh[l].shape[2]]
+            assert np.array_equal(got.view(np.uint32), fresh[l].view(np.uint32)), f"sequence {b}, level {l}"
+            np.testing.assert_allclose(got, want[l], rtol=2.0 ** -22, atol=0.0)
