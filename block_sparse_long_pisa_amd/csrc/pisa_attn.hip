@@ -32,7 +32,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
                                                             const uint16_t* __restrict__ v,
                                                             const int32_t* __restrict__ idx,
                                                             const int32_t* __restrict__ cnt, uint16_t* __restrict__ out,
-                                                            float* __restrict__ lse, int parts) {
+                                                            float* __restrict__ lse, int parts, int slab_major) {
   constexpr int NT = NW * 64;
   // two stages of K and V tiles, filled by asynchronous copies
   __shared__ __attribute__((aligned(16))) uint16_t K0[TilePitch<D, BS>::KSIZE];
@@ -42,14 +42,25 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
   __shared__ int sel[kMaxTopK];
 
   // Persistent: workgroup i takes the (unit, part) items i, i + gridDim.x, ...
-  // Items are ordered heaviest units first, and consecutive items walk the
-  // (batch, kv head) slabs, so that one slab's items land on one XCD.
+  // Items are ordered heaviest units first. Either consecutive items walk the
+  // (batch, kv head) slabs, so that one slab's items land on one XCD (few slabs,
+  // large units), or (slab_major) all of one slab's items come before the next
+  // slab's, so that the workgroups in flight read one slab's keys and values
+  // and those stay in the caches (many slabs, small units).
   const int slabs = g.B * g.Hkv;
   const int64_t items = (int64_t)g.nb * slabs * parts;
   for (int64_t wg = blockIdx.x; wg < items; wg += gridDim.x) {
-    const int slab = (int)(wg % slabs);
-    const int part = (int)((wg / slabs) % parts);
-    const int qb = g.nb - 1 - (int)(wg / ((int64_t)slabs * parts));
+    int slab, part, qb;
+    if (slab_major) {
+      const int64_t per_slab = (int64_t)g.nb * parts;
+      slab = (int)(wg / per_slab);
+      part = (int)(wg % parts);
+      qb = g.nb - 1 - (int)((wg % per_slab) / parts);
+    } else {
+      slab = (int)(wg % slabs);
+      part = (int)((wg / slabs) % parts);
+      qb = g.nb - 1 - (int)(wg / ((int64_t)slabs * parts));
+    }
     const int64_t unit = (int64_t)slab * g.nb + qb;
     const int nsel = min(max(cnt[unit], 0), g.K);
     for (int t = threadIdx.x; t < nsel; t += NT) sel[t] = idx[unit * g.K + t];
@@ -145,8 +156,12 @@ hipError_t launch_bf16(const Geo& g, const void* q, const void* k, const void* v
   hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;
   const int64_t grid = std::min<int64_t>(items, (int64_t)kAttnWgPerCu * cus);
+  // many slabs: all of one slab's items first (its keys and values stay cached);
+  // few: slab-fastest, one slab per XCD
+  const int slab_major = g.B * g.Hkv > 8 ? 1 : 0;
   hipLaunchKernelGGL((attn_bf16_kernel<D, BS, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, g,
-                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, (uint16_t*)out, lse, parts);
+                     (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, (uint16_t*)out, lse, parts,
+                     slab_major);
   return hipGetLastError();
 }
 

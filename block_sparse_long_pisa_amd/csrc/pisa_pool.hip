@@ -242,14 +242,16 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
 // All levels from 2 up in one launch: a workgroup owns one top-level node and
 // builds its subtree level by level from the level-1 summaries. Within a level
 // each thread folds NM nodes of one column, and all F x NM child loads of a
-// round are issued before any is used.
-constexpr int kUpperThreads = 256;
+// round are issued before any is used. 1024 threads: a subtree of up to
+// 8 * 64 / F level-2 nodes (d = 128) takes a single round of loads, so even a
+// slab whose top level holds two nodes builds in a few dependent steps.
+constexpr int kUpperThreads = 1024;
 
 template <int D, bool MX, int F>
 __global__ __launch_bounds__(kUpperThreads) void pool_upper_kernel(Geo g, float* __restrict__ pyr) {
   using PO = Pool<MX>;
   constexpr int CPT = kUpperThreads / D;  // node groups per column
-  constexpr int NM = 64 / F;              // nodes a thread folds per round
+  constexpr int NM = F >= 4 ? 64 / F : 16;  // nodes a thread folds per round
   const int top = blockIdx.x;
   const int slab = blockIdx.y;
   float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
