@@ -26,19 +26,28 @@
 namespace pisa {
 namespace {
 
+#ifndef PISA_ATTN_SMALL_ST
+#define PISA_ATTN_SMALL_ST 1
+#endif
+// Workgroups of at most two waves (units of at most 64 query rows): one stage of
+// K/V tiles and at most 256 registers per wave, so that four workgroups -- two
+// waves per SIMD -- share a compute unit.
+template <int NW>
+constexpr int kStages = NW <= 2 ? PISA_ATTN_SMALL_ST : 2;
+
 template <int D, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2 && PISA_ATTN_SMALL_ST == 1 ? 2 : 1))) void attn_bf16_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v,
                                                             const int32_t* __restrict__ idx,
                                                             const int32_t* __restrict__ cnt, uint16_t* __restrict__ out,
                                                             float* __restrict__ lse, int parts, int slab_major) {
   constexpr int NT = NW * 64;
-  // two stages of K and V tiles, filled by asynchronous copies
+  // kStages<NW> stages of K and V tiles, filled by asynchronous copies
   __shared__ __attribute__((aligned(16))) uint16_t K0[TilePitch<D, BS>::KSIZE];
   __shared__ __attribute__((aligned(16))) uint16_t V0[TilePitch<D, BS>::VSIZE];
-  __shared__ __attribute__((aligned(16))) uint16_t K1[TilePitch<D, BS>::KSIZE];
-  __shared__ __attribute__((aligned(16))) uint16_t V1[TilePitch<D, BS>::VSIZE];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[kStages<NW> == 2 ? TilePitch<D, BS>::KSIZE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[kStages<NW> == 2 ? TilePitch<D, BS>::VSIZE : 8];
   __shared__ int sel[kMaxTopK];
 
   // Persistent: workgroup i takes the (unit, part) items i, i + gridDim.x, ...
@@ -49,10 +58,20 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
   // and those stay in the caches (many slabs, small units).
   const int slabs = g.B * g.Hkv;
   const int64_t items = (int64_t)g.nb * slabs * parts;
-  for (int64_t wg = blockIdx.x; wg < items; wg += gridDim.x) {
+  // order 2: workgroup i runs on XCD i % 8 (round-robin placement), and each XCD
+  // walks its own slabs (x, x + 8, ...) one after another, so that one XCD's
+  // L2 sees one slab's keys and values at a time
+  const int64_t per_slab = (int64_t)g.nb * parts;
+  const int64_t first = slab_major == 2 ? blockIdx.x / 8 : blockIdx.x;
+  const int64_t stride = slab_major == 2 ? gridDim.x / 8 : gridDim.x;
+  const int64_t count = slab_major == 2 ? items / 8 : items;
+  for (int64_t wg = first; wg < count; wg += stride) {
     int slab, part, qb;
-    if (slab_major) {
-      const int64_t per_slab = (int64_t)g.nb * parts;
+    if (slab_major == 2) {
+      slab = (int)(blockIdx.x % 8) + 8 * (int)(wg / per_slab);
+      part = (int)(wg % parts);
+      qb = g.nb - 1 - (int)((wg % per_slab) / parts);
+    } else if (slab_major) {
       slab = (int)(wg / per_slab);
       part = (int)(wg % parts);
       qb = g.nb - 1 - (int)((wg % per_slab) / parts);
@@ -65,7 +84,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(Geo g, const uint16_
     const int nsel = min(max(cnt[unit], 0), g.K);
     for (int t = threadIdx.x; t < nsel; t += NT) sel[t] = idx[unit * g.K + t];
     __syncthreads();
-    attend_unit<D, BS, NW>(g, q, k, v, out, lse, slab, part, qb, sel, nsel, K0, V0, K1, V1);
+    attend_unit<D, BS, NW, kStages<NW>>(g, q, k, v, out, lse, slab, part, qb, sel, nsel, K0, V0, K1, V1);
     __syncthreads();  // every wave is done with sel and the stages before the next item
   }
 }
@@ -158,7 +177,12 @@ hipError_t launch_bf16(const Geo& g, const void* q, const void* k, const void* v
   const int64_t grid = std::min<int64_t>(items, (int64_t)kAttnWgPerCu * cus);
   // many slabs: all of one slab's items first (its keys and values stay cached);
   // few: slab-fastest, one slab per XCD
+#ifndef PISA_ATTN_ORDER
   const int slab_major = g.B * g.Hkv > 8 ? 1 : 0;
+#else
+  const int slab_major = PISA_ATTN_ORDER == 2 ? ((g.B * g.Hkv) % 8 == 0 && grid % 8 == 0 ? 2 : 1)
+                                              : PISA_ATTN_ORDER;
+#endif
   hipLaunchKernelGGL((attn_bf16_kernel<D, BS, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, g,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, (uint16_t*)out, lse, parts,
                      slab_major);

@@ -68,6 +68,10 @@ struct TileWalk {
       nvalid = local_rows;
       local = causal;
     }
+    // every lane reads the same selection entry: make the block and its key
+    // count scalar, so tile addresses are formed once per tile in scalar registers
+    j = __builtin_amdgcn_readfirstlane(j);
+    nvalid = __builtin_amdgcn_readfirstlane(nvalid);
   }
 };
 
@@ -122,22 +126,29 @@ __device__ __forceinline__ int unit_src(int u, int rows) {
   return min(r, rows - 1) * D + (cu < D / 8 ? cu : 0) * 8;
 }
 
-// Per-lane source offsets of this wave's copies of a full tile (they do not
-// change from tile to tile).
+// Per-lane source offsets, in bytes, of this wave's copies of a full tile
+// (they do not change from tile to tile).
 template <int D, int BS, int NW>
 struct DmaPlan {
   using TP = TilePitch<D, BS>;
   static constexpr int KN = (TP::KI + NW - 1) / NW;
   static constexpr int VN = (TP::VI + NW - 1) / NW;
-  int k[KN];
-  int v[VN];
+  uint32_t k[KN];
+  uint32_t v[VN];
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int n = 0; n < KN; ++n) k[n] = unit_src<D, TP::KU>((wave + NW * n) * 64 + lane, BS);
+    for (int n = 0; n < KN; ++n) k[n] = 2u * unit_src<D, TP::KU>((wave + NW * n) * 64 + lane, BS);
 #pragma unroll
-    for (int n = 0; n < VN; ++n) v[n] = unit_src<D, TP::VU>((wave + NW * n) * 64 + lane, BS);
+    for (int n = 0; n < VN; ++n) v[n] = 2u * unit_src<D, TP::VU>((wave + NW * n) * 64 + lane, BS);
   }
 };
+
+// One 16-byte copy per lane from a wave-uniform base plus this lane's 32-bit
+// byte offset: the address form whose base sits in scalar registers, so that a
+// copy costs no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, uint16_t* dst) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(base) + off, (lds_void_ptr)dst, 16, 0, 0);
+}
 
 // Issue the asynchronous global->LDS copies of one K and one V tile (block j).
 // Each wave instruction fills 64 consecutive 16-byte LDS units in row order.
@@ -147,24 +158,27 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kt, cons
                                            const DmaPlan<D, BS, NW>& plan) {
   using TP = TilePitch<D, BS>;
   using PL = DmaPlan<D, BS, NW>;
+  if (rows_in_mem == BS) {  // uniform: a whole block, the planned offsets as they are
+#pragma unroll
+    for (int n = 0; n < PL::KN; ++n)
+      if (wave + NW * n < TP::KI) copy16_to_lds(kt, plan.k[n], kdst + (wave + NW * n) * 512);
+#pragma unroll
+    for (int n = 0; n < PL::VN; ++n)
+      if (wave + NW * n < TP::VI) copy16_to_lds(vt, plan.v[n], vdst + (wave + NW * n) * 512);
+    return;
+  }
   // a planned offset row * D + col keeps its column; rows past the last valid
   // one (only in a sequence's ragged last block) move to the last valid row
-  const int last = (rows_in_mem - 1) * D;
+  const uint32_t last = (uint32_t)(rows_in_mem - 1) * D * 2;
 #pragma unroll
   for (int n = 0; n < PL::KN; ++n) {
     const int i = wave + NW * n;
-    if (i < TP::KI) {
-      const int off = min(plan.k[n], last + (plan.k[n] & (D - 1)));
-      __builtin_amdgcn_global_load_lds(kt + off, (lds_void_ptr)(kdst + i * 512), 16, 0, 0);
-    }
+    if (i < TP::KI) copy16_to_lds(kt, min(plan.k[n], last + (plan.k[n] & (2 * D - 1))), kdst + i * 512);
   }
 #pragma unroll
   for (int n = 0; n < PL::VN; ++n) {
     const int i = wave + NW * n;
-    if (i < TP::VI) {
-      const int off = min(plan.v[n], last + (plan.v[n] & (D - 1)));
-      __builtin_amdgcn_global_load_lds(vt + off, (lds_void_ptr)(vdst + i * 512), 16, 0, 0);
-    }
+    if (i < TP::VI) copy16_to_lds(vt, min(plan.v[n], last + (plan.v[n] & (2 * D - 1))), vdst + i * 512);
   }
 }
 

@@ -117,8 +117,11 @@ __device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_
 
 // One (unit, part) of the bf16 attention: the tile walk over the selected
 // blocks sel[0, nsel) (in LDS, visible to every wave), through two stages of K/V
-// tiles in LDS (K0/V0 and K1/V1).
-template <int D, int BS, int NW>
+// tiles in LDS (K0/V0 and K1/V1), or with ST = 1 through one stage (K0/V0; K1
+// and V1 unused): each tile's copy then waits for the previous tile's products,
+// and the other workgroups that the smaller LDS footprint lets share the compute
+// unit cover that wait.
+template <int D, int BS, int NW, int ST = 2>
 __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __restrict__ q,
                                             const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                             uint16_t* __restrict__ out, float* __restrict__ lse, int slab, int part,
@@ -173,6 +176,17 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
   walk.at(0, sel, g, qb, local_rows, j, nvalid, local);
   issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
                         wave, lane, plan);
+  if constexpr (ST == 1) {
+    for (int t = 0; t < walk.ntiles; ++t) {
+      wait_loads_and_sync();
+      compute_tile<D, BS>(st, K0, V0, nvalid, local, j * BS, qpos, hi, c, wg_qmax);
+      if (t + 1 >= walk.ntiles) break;
+      __syncthreads();  // every wave is done with the stage before it is refilled
+      walk.at(t + 1, sel, g, qb, local_rows, j, nvalid, local);
+      issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0,
+                            V0, wave, lane, plan);
+    }
+  } else
   for (int t = 0; t < walk.ntiles; t += 2) {
     // even tile: compute from stage 0 while stage 1 fills
     wait_loads_and_sync();
