@@ -14,7 +14,8 @@
 // (batch, kv head, query block) unit -- rows of all heads in the GQA group --
 // so every K/V tile staged in LDS feeds up to 256 rows. Tiles arrive by
 // asynchronous global->LDS copies into two stages, the next tile in flight while
-// the current one is computed. Per tile each wave computes S^T = K Q^T with
+// the current one is computed (units of at most 64 rows: one stage, four
+// workgroups per compute unit covering each other's copies). Per tile each wave computes S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (a lane then owns one query column), runs the
 // online softmax in registers, and accumulates O^T += V^T P^T on the same
 // matrix cores, reading V^T fragments with gfx950's transposing LDS reads.
@@ -26,17 +27,14 @@
 namespace pisa {
 namespace {
 
-#ifndef PISA_ATTN_SMALL_ST
-#define PISA_ATTN_SMALL_ST 1
-#endif
 // Workgroups of at most two waves (units of at most 64 query rows): one stage of
 // K/V tiles and at most 256 registers per wave, so that four workgroups -- two
 // waves per SIMD -- share a compute unit.
 template <int NW>
-constexpr int kStages = NW <= 2 ? PISA_ATTN_SMALL_ST : 2;
+constexpr int kStages = NW <= 2 ? 1 : 2;
 
 template <int D, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2 && PISA_ATTN_SMALL_ST == 1 ? 2 : 1))) void attn_bf16_kernel(Geo g, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2 ? 2 : 1))) void attn_bf16_kernel(Geo g, const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v,
                                                             const int32_t* __restrict__ idx,
@@ -58,20 +56,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2
   // and those stay in the caches (many slabs, small units).
   const int slabs = g.B * g.Hkv;
   const int64_t items = (int64_t)g.nb * slabs * parts;
-  // order 2: workgroup i runs on XCD i % 8 (round-robin placement), and each XCD
-  // walks its own slabs (x, x + 8, ...) one after another, so that one XCD's
-  // L2 sees one slab's keys and values at a time
-  const int64_t per_slab = (int64_t)g.nb * parts;
-  const int64_t first = slab_major == 2 ? blockIdx.x / 8 : blockIdx.x;
-  const int64_t stride = slab_major == 2 ? gridDim.x / 8 : gridDim.x;
-  const int64_t count = slab_major == 2 ? items / 8 : items;
-  for (int64_t wg = first; wg < count; wg += stride) {
+  for (int64_t wg = blockIdx.x; wg < items; wg += gridDim.x) {
     int slab, part, qb;
-    if (slab_major == 2) {
-      slab = (int)(blockIdx.x % 8) + 8 * (int)(wg / per_slab);
-      part = (int)(wg % parts);
-      qb = g.nb - 1 - (int)((wg % per_slab) / parts);
-    } else if (slab_major) {
+    if (slab_major) {
+      const int64_t per_slab = (int64_t)g.nb * parts;
       slab = (int)(wg / per_slab);
       part = (int)(wg % parts);
       qb = g.nb - 1 - (int)((wg % per_slab) / parts);
@@ -177,12 +165,9 @@ hipError_t launch_bf16(const Geo& g, const void* q, const void* k, const void* v
   const int64_t grid = std::min<int64_t>(items, (int64_t)kAttnWgPerCu * cus);
   // many slabs: all of one slab's items first (its keys and values stay cached);
   // few: slab-fastest, one slab per XCD
-#ifndef PISA_ATTN_ORDER
+  // many slabs: all of one slab's items first (its keys and values stay cached);
+  // few: slab-fastest, one slab per XCD
   const int slab_major = g.B * g.Hkv > 8 ? 1 : 0;
-#else
-  const int slab_major = PISA_ATTN_ORDER == 2 ? ((g.B * g.Hkv) % 8 == 0 && grid % 8 == 0 ? 2 : 1)
-                                              : PISA_ATTN_ORDER;
-#endif
   hipLaunchKernelGGL((attn_bf16_kernel<D, BS, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, g,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, (uint16_t*)out, lse, parts,
                      slab_major);
