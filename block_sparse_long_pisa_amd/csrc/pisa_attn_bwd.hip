@@ -94,19 +94,19 @@ struct DqPlan {
   static constexpr int VN = (TP::KI + NW - 1) / NW;
   static constexpr int KCOP = KL::SIZE / 512;  // whole 1 KB copies of the K tile
   static constexpr int KN = (KCOP + NW - 1) / NW;
-  int v[VN];
-  int k[KN];
+  uint32_t v[VN];  // byte offsets
+  uint32_t k[KN];
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int n = 0; n < VN; ++n) v[n] = unit_src<D, TP::KU>((wave + NW * n) * 64 + lane, BS);
+    for (int n = 0; n < VN; ++n) v[n] = 2u * unit_src<D, TP::KU>((wave + NW * n) * 64 + lane, BS);
 #pragma unroll
     for (int n = 0; n < KN; ++n) {
       const int p = (wave + NW * n) * 64 + lane;
       if (KL::kSwz) {
         const int r = p / (D / 8);
-        k[n] = r * D + (((p % (D / 8)) ^ dq_swz(r)) * 8);
+        k[n] = 2u * (r * D + (((p % (D / 8)) ^ dq_swz(r)) * 8));
       } else {
-        k[n] = unit_src<D, TP::VU>(p, BS);
+        k[n] = 2u * unit_src<D, TP::VU>(p, BS);
       }
     }
   }
@@ -119,22 +119,21 @@ __device__ __forceinline__ void issue_dq_tile(const uint16_t* __restrict__ vt, c
                                               int rows_in_mem, uint16_t* vdst, uint16_t* kdst, int wave, int lane,
                                               const DqPlan<D, BS, NW>& plan) {
   using PL = DqPlan<D, BS, NW>;
-  const int last = (rows_in_mem - 1) * D;
+  // a whole block takes the planned offsets as they are (uniform test); in a
+  // ragged last block, rows past the last valid one move to it
+  const bool whole = rows_in_mem == BS;
+  const uint32_t last = (uint32_t)(rows_in_mem - 1) * D * 2;
 #pragma unroll
   for (int n = 0; n < PL::VN; ++n) {
     const int i = wave + NW * n;
-    if (i < TilePitch<D, BS>::KI) {
-      const int off = min(plan.v[n], last + (plan.v[n] & (D - 1)));
-      __builtin_amdgcn_global_load_lds(vt + off, (lds_void_ptr)(vdst + i * 512), 16, 0, 0);
-    }
+    if (i < TilePitch<D, BS>::KI)
+      copy16_to_lds(vt, whole ? plan.v[n] : min(plan.v[n], last + (plan.v[n] & (2 * D - 1))), vdst + i * 512);
   }
 #pragma unroll
   for (int n = 0; n < PL::KN; ++n) {
     const int i = wave + NW * n;
-    if (i < PL::KCOP) {
-      const int off = min(plan.k[n], last + (plan.k[n] & (D - 1)));
-      __builtin_amdgcn_global_load_lds(kt + off, (lds_void_ptr)(kdst + i * 512), 16, 0, 0);
-    }
+    if (i < PL::KCOP)
+      copy16_to_lds(kt, whole ? plan.k[n] : min(plan.k[n], last + (plan.k[n] & (2 * D - 1))), kdst + i * 512);
   }
 }
 
@@ -458,13 +457,13 @@ template <int D, int BS, int NW>
 struct KvPlan {
   static constexpr int UPR = D / 8;
   static constexpr int NC = BS * UPR / 64 / NW;
-  int src[NC];
+  uint32_t src[NC];  // bytes
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
       const int p = (wave + NW * n) * 64 + lane;  // physical unit of the tile
       const int r = p / UPR;
-      src[n] = r * D + (((p % UPR) ^ kv_swz<D>(r)) * 8);
+      src[n] = 2u * (r * D + (((p % UPR) ^ kv_swz<D>(r)) * 8));
     }
   }
 };
@@ -480,22 +479,25 @@ __device__ __forceinline__ void issue_kv_rows(const Geo& g, const uint16_t* q, c
   using PL = KvPlan<D, BS, NW>;
   const int64_t r0 = ((int64_t)b * g.Hq + h) * g.N + (int64_t)qb * BS;
   const int rows = min(BS, g.N - qb * BS);
-  const int last = (rows - 1) * D;
+  const uint32_t last = (uint32_t)(rows - 1) * D * 2;
+  const bool whole = rows == BS;  // uniform: the planned offsets as they are
   const uint16_t* qt = q + r0 * D;
   const uint16_t* ot = dout + r0 * D;
 #pragma unroll
   for (int n = 0; n < PL::NC; ++n) {
-    const int off = min(plan.src[n], last + (plan.src[n] & (D - 1)));
+    const uint32_t off = whole ? plan.src[n] : min(plan.src[n], last + (plan.src[n] & (2 * D - 1)));
     const int i = wave + NW * n;
-    __builtin_amdgcn_global_load_lds(qt + off, (lds_void_ptr)(qdst + i * 512), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(ot + off, (lds_void_ptr)(odst + i * 512), 16, 0, 0);
+    copy16_to_lds(qt, off, qdst + i * 512);
+    copy16_to_lds(ot, off, odst + i * 512);
   }
 #pragma unroll
   for (int n = 0; n < (BS + 63) / 64; ++n) {
     if (n % NW == wave) {
-      const int r = min(n * 64 + lane, rows - 1);
-      __builtin_amdgcn_global_load_lds(lse2 + r0 + r, (lds_void_ptr)(ldst + n * 64), 4, 0, 0);
-      __builtin_amdgcn_global_load_lds(rowdot + r0 + r, (lds_void_ptr)(rdst + n * 64), 4, 0, 0);
+      const uint32_t r = (uint32_t)min(n * 64 + lane, rows - 1);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(lse2 + r0) + 4 * r, (lds_void_ptr)(ldst + n * 64),
+                                       4, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(rowdot + r0) + 4 * r,
+                                       (lds_void_ptr)(rdst + n * 64), 4, 0, 0);
     }
   }
 }
@@ -671,7 +673,8 @@ __global__ __launch_bounds__(BS / 16 * 64) void bwd_kv_kernel(Geo g, const uint1
   plan.init(wave, lane);
 
   auto entry = [&](int t, int& qb, int& h, int& kind) {
-    const int e = lists[e0 + t / g.G];
+    // one list entry for every lane: scalar, so row addresses form in scalar registers
+    const int e = __builtin_amdgcn_readfirstlane(lists[e0 + t / g.G]);
     qb = e & 0x0fffffff;
     kind = e >> 28;
     h = kvh * g.G + t % g.G;
