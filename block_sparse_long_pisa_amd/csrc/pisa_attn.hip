@@ -39,7 +39,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2
                                                             const uint16_t* __restrict__ v,
                                                             const int32_t* __restrict__ idx,
                                                             const int32_t* __restrict__ cnt, uint16_t* __restrict__ out,
-                                                            float* __restrict__ lse, int parts, int slab_major) {
+                                                            float* __restrict__ lse, int parts, int order) {
   constexpr int NT = NW * 64;
   // kStages<NW> stages of K and V tiles, filled by asynchronous copies
   __shared__ __attribute__((aligned(16))) uint16_t K0[TilePitch<D, BS>::KSIZE];
@@ -48,18 +48,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2
   __shared__ __attribute__((aligned(16))) uint16_t V1[kStages<NW> == 2 ? TilePitch<D, BS>::VSIZE : 8];
   __shared__ int sel[kMaxTopK];
 
-  // Persistent: workgroup i takes the (unit, part) items i, i + gridDim.x, ...
-  // Items are ordered heaviest units first. Either consecutive items walk the
-  // (batch, kv head) slabs, so that one slab's items land on one XCD (few slabs,
-  // large units), or (slab_major) all of one slab's items come before the next
-  // slab's, so that the workgroups in flight read one slab's keys and values
-  // and those stay in the caches (many slabs, small units).
+  // Persistent: each workgroup takes every gridDim.x-th (unit, part) item of its
+  // list, heaviest units (latest query blocks) first. order 2: workgroup i runs
+  // on XCD i % 8 (round-robin placement) and takes only the slabs x, x + 8, ...
+  // of its XCD x, one slab after another, so that an XCD's L2 holds the keys and
+  // values of one slab at a time. order 1: all of one slab's items before the
+  // next slab's, over the whole GPU. order 0: consecutive items walk the slabs.
   const int slabs = g.B * g.Hkv;
   const int64_t items = (int64_t)g.nb * slabs * parts;
-  for (int64_t wg = blockIdx.x; wg < items; wg += gridDim.x) {
+  const int64_t per_slab = (int64_t)g.nb * parts;
+  const int64_t first = order == 2 ? blockIdx.x / 8 : blockIdx.x;
+  const int64_t stride = order == 2 ? gridDim.x / 8 : gridDim.x;
+  const int64_t count = order == 2 ? items / 8 : items;
+  for (int64_t wg = first; wg < count; wg += stride) {
     int slab, part, qb;
-    if (slab_major) {
-      const int64_t per_slab = (int64_t)g.nb * parts;
+    if (order == 2) {
+      slab = (int)(blockIdx.x % 8) + 8 * (int)(wg / per_slab);
+      part = (int)(wg % parts);
+      qb = g.nb - 1 - (int)((wg % per_slab) / parts);
+    } else if (order == 1) {
       slab = (int)(wg / per_slab);
       part = (int)(wg % parts);
       qb = g.nb - 1 - (int)((wg % per_slab) / parts);
@@ -163,14 +170,14 @@ hipError_t launch_bf16(const Geo& g, const void* q, const void* k, const void* v
   hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;
   const int64_t grid = std::min<int64_t>(items, (int64_t)kAttnWgPerCu * cus);
-  // many slabs: all of one slab's items first (its keys and values stay cached);
-  // few: slab-fastest, one slab per XCD
-  // many slabs: all of one slab's items first (its keys and values stay cached);
-  // few: slab-fastest, one slab per XCD
-  const int slab_major = g.B * g.Hkv > 8 ? 1 : 0;
+  // item order: slabs divisible among the 8 XCDs -- each XCD walks its own
+  // slabs, one after another (2); otherwise many slabs -- one slab after another
+  // over the whole GPU (1); few -- slab-fastest (0)
+  const int slabs = g.B * g.Hkv;
+  const int order = slabs % 8 == 0 && grid % 8 == 0 ? 2 : slabs > 8 ? 1 : 0;
   hipLaunchKernelGGL((attn_bf16_kernel<D, BS, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, g,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, (uint16_t*)out, lse, parts,
-                     slab_major);
+                     order);
   return hipGetLastError();
 }
 
