@@ -182,6 +182,36 @@ __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kt, cons
   }
 }
 
+// Issue the copies of one half of a tile: its keys (KEYS) or its values.
+template <int D, int BS, int NW, bool KEYS>
+__device__ __forceinline__ void issue_half(const uint16_t* __restrict__ src, int rows_in_mem, uint16_t* dst,
+                                           int wave, const DmaPlan<D, BS, NW>& plan) {
+  using TP = TilePitch<D, BS>;
+  using PL = DmaPlan<D, BS, NW>;
+  constexpr int N = KEYS ? PL::KN : PL::VN;
+  constexpr int I = KEYS ? TP::KI : TP::VI;
+  const uint32_t* off = KEYS ? plan.k : plan.v;
+  const bool whole = rows_in_mem == BS;  // uniform: a whole block takes the planned offsets as they are
+  const uint32_t last = (uint32_t)(rows_in_mem - 1) * D * 2;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int i = wave + NW * n;
+    if (i < I) copy16_to_lds(src, whole ? off[n] : min(off[n], last + (off[n] & (2 * D - 1))), dst + i * 512);
+  }
+}
+
+// Wait until at most N of this wave's vector memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14));  // expcnt, lgkmcnt left free
+}
+
+// A workgroup barrier after which every wave's LDS reads have completed. Unlike
+// __syncthreads(), whose fence also waits for this wave's copies into LDS still
+// in flight, it leaves those copies running.
+__device__ __forceinline__ void lds_read_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ void wait_loads_and_sync() {
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0) only (expcnt, lgkmcnt left free)
   __syncthreads();                            // ... and every other wave's

@@ -22,96 +22,121 @@ struct AttnState {
   int offv;      // byte offset of this lane's first V^T transposing read in a V tile
 };
 
-// One key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T, in chunks of
-// at most 64 keys (32 live accumulator registers for S per chunk).
+// Keys per chunk of a tile: the scores of at most 64 keys (32 live accumulator
+// registers) are held at a time.
+template <int BS>
+constexpr int kChunk = BS < 64 ? BS : 64;
+
+// S^T = K Q^T for the keys [ch * KC, ch * KC + KC) of the tile in `ks`, with the
+// keys beyond `nvalid` (partial block) and after the query (causal diagonal)
+// masked.
+template <int D, int BS>
+__device__ __forceinline__ void tile_scores(const AttnState<D, BS>& st, const uint16_t* ks, int ch, int nvalid,
+                                            bool local, int key0, int qpos, int hi,
+                                            f32x16_t (&sacc)[kChunk<BS> / 32]) {
+  constexpr int NDS = D / 16;
+  constexpr int KC = kChunk<BS>;
+  constexpr int NKB = KC / 32;
+  const char* kb_base = reinterpret_cast<const char*>(ks);
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb_base + st.offk + ds * 32 +
+                                                            (ch * KC + kb * 32) * TilePitch<D>::K * 2);
+      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[ds], sacc[kb], 0, 0, 0);
+    }
+  }
+  if (__builtin_expect(local || nvalid < BS, 0)) {  // uniform across the workgroup
+    // keys of this tile beyond `lim` are masked (partial block, causal diagonal)
+    const int lim = min(nvalid - 1, local ? qpos - key0 : BS - 1) - (ch * KC + hi * 4);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -__builtin_inff();
+  }
+}
+
+// Online softmax of one chunk's scores and O^T += V^T P^T with the chunk's
+// values from the tile in `vs`.
+template <int D, int BS>
+__device__ __forceinline__ void tile_update(AttnState<D, BS>& st, f32x16_t (&sacc)[kChunk<BS> / 32],
+                                            const uint16_t* vs, int ch, float c) {
+  constexpr int NDB = D / 32;
+  constexpr int KC = kChunk<BS>;
+  constexpr int NKB = KC / 32;
+  const char* vb_base = reinterpret_cast<const char*>(vs);
+  // online softmax in the log2 domain; the reference max only moves when the
+  // chunk max exceeds it by more than 8 (a factor 2^8), then O and l rescale
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+  mx = max_halves(mx);
+  const float mt = mx * c;
+  const bool move = mt > st.m_run + 8.f;
+  const float m_ref = move ? mt : st.m_run;
+  const float m_use = m_ref == -__builtin_inff() ? 0.f : m_ref;
+  if (__any(move)) {
+    const float alpha = fast_exp2(st.m_run - m_use);
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) st.oacc[db][i] *= alpha;
+  }
+  st.m_run = m_ref;
+  float rs = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(fmaf(sacc[kb][i], c, -m_use));
+      sacc[kb][i] = p;
+      rs += p;
+    }
+  // O^T[d][query] += V^T P^T over 16-key steps; slot (hi, e) of step (kb, hh)
+  // holds key kb*32 + hh*16 + (e/4)*8 + hi*4 + e%4
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x8_t pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][hh * 8 + e];
+      const int step = (ch * KC + kb * 32 + hh * 16) * TilePitch<D>::V * 2;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_ptr)(vb_base + st.offv + step + db * 64));
+        const v4i16_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_ptr)(vb_base + st.offv + step + db * 64 + 8 * TilePitch<D>::V * 2));
+        const v4i16_t a8[2] = {lo, up};
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a8);
+        st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, st.oacc[db], 0, 0, 0);
+      }
+    }
+  }
+  st.l_run += sum_halves(rs);
+}
+
+// One key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T, chunk by chunk.
 template <int D, int BS>
 __device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_t* ks, const uint16_t* vs, int nvalid,
                                              bool local, int key0, int qpos, int hi, float c, int wg_qmax) {
-  constexpr int CPR = D / 8;
-  constexpr int NDS = D / 16, NDB = D / 32;
-  constexpr int KC = BS < 64 ? BS : 64;  // keys per chunk
-  constexpr int NKB = KC / 32;
-  const char* kb_base = reinterpret_cast<const char*>(ks);
-  const char* vb_base = reinterpret_cast<const char*>(vs);
+  constexpr int KC = kChunk<BS>;
 #pragma unroll
   for (int ch = 0; ch < BS / KC; ++ch) {
     // a chunk past the valid keys, or wholly after the workgroup's last query on
     // the causal diagonal, contributes nothing to any row (uniform test)
     if (ch > 0 && (ch * KC >= nvalid || (local && key0 + ch * KC > wg_qmax))) break;
-    f32x16_t sacc[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb_base + st.offk + ds * 32 +
-                                                              (ch * KC + kb * 32) * TilePitch<D>::K * 2);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[ds], sacc[kb], 0, 0, 0);
-      }
-    }
-    if (__builtin_expect(local || nvalid < BS, 0)) {  // uniform across the workgroup
-      // keys of this tile beyond `lim` are masked (partial block, causal diagonal)
-      const int lim = min(nvalid - 1, local ? qpos - key0 : BS - 1) - (ch * KC + hi * 4);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sacc[kb][i] = -__builtin_inff();
-    }
-    // online softmax in the log2 domain; the reference max only moves when the
-    // chunk max exceeds it by more than 8 (a factor 2^8), then O and l rescale
-    float mx = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = max_halves(mx);
-    const float mt = mx * c;
-    const bool move = mt > st.m_run + 8.f;
-    const float m_ref = move ? mt : st.m_run;
-    const float m_use = m_ref == -__builtin_inff() ? 0.f : m_ref;
-    if (__any(move)) {
-      const float alpha = fast_exp2(st.m_run - m_use);
-      st.l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st.oacc[db][i] *= alpha;
-    }
-    st.m_run = m_ref;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(sacc[kb][i], c, -m_use));
-        sacc[kb][i] = p;
-        rs += p;
-      }
-    // O^T[d][query] += V^T P^T over 16-key steps; slot (hi, e) of step (kb, hh)
-    // holds key kb*32 + hh*16 + (e/4)*8 + hi*4 + e%4
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        bf16x8_t pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][hh * 8 + e];
-        const int step = (ch * KC + kb * 32 + hh * 16) * TilePitch<D>::V * 2;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_ptr)(vb_base + st.offv + step + db * 64));
-          const v4i16_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_v4i16_ptr)(vb_base + st.offv + step + db * 64 + 8 * TilePitch<D>::V * 2));
-          const v4i16_t a8[2] = {lo, up};
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a8);
-          st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, st.oacc[db], 0, 0, 0);
-        }
-      }
-    }
-    st.l_run += sum_halves(rs);
+    f32x16_t sacc[KC / 32];
+    tile_scores<D, BS>(st, ks, ch, nvalid, local, key0, qpos, hi, sacc);
+    tile_update<D, BS>(st, sacc, vs, ch, c);
   }
 }
 
@@ -177,14 +202,34 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
   issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
                         wave, lane, plan);
   if constexpr (ST == 1) {
+    // One stage, split by phase: the keys of tile t + 1 load while tile t's
+    // softmax and value product run, its values while tile t + 1's scores run.
+    // Each wave's copies complete in the order issued (K before V), so waiting
+    // until at most VMIN of its copies are outstanding -- fewer than the V
+    // copies it issued after them -- means its K copies have landed.
+    static_assert(BS <= 64, "a one-stage tile is one chunk of keys");
+    constexpr int VMIN = TilePitch<D, BS>::VI / NW;
     for (int t = 0; t < walk.ntiles; ++t) {
-      wait_loads_and_sync();
-      compute_tile<D, BS>(st, K0, V0, nvalid, local, j * BS, qpos, hi, c, wg_qmax);
-      if (t + 1 >= walk.ntiles) break;
-      __syncthreads();  // every wave is done with the stage before it is refilled
-      walk.at(t + 1, sel, g, qb, local_rows, j, nvalid, local);
-      issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0,
-                            V0, wave, lane, plan);
+      wait_loads<VMIN>();
+      __syncthreads();  // K(t) has landed for every wave
+      f32x16_t sacc[BS / 32];
+      tile_scores<D, BS>(st, K0, 0, nvalid, local, j * BS, qpos, hi, sacc);
+      wait_loads<0>();
+      __syncthreads();  // V(t) has landed; every wave is done with K(t)
+      const bool more = t + 1 < walk.ntiles;
+      int j1 = j, nv1 = 0;
+      bool loc1 = false;
+      if (more) {
+        walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
+        issue_half<D, BS, NW, true>(kbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K0, wave, plan);
+      }
+      tile_update<D, BS>(st, sacc, V0, 0, c);
+      if (!more) break;
+      lds_read_barrier();  // every wave is done with V(t); K(t + 1) keeps loading
+      issue_half<D, BS, NW, false>(vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), V0, wave, plan);
+      j = j1;
+      nvalid = nv1;
+      local = loc1;
     }
   } else
   for (int t = 0; t < walk.ntiles; t += 2) {
