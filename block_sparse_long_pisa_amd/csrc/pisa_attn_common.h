@@ -150,39 +150,19 @@ __device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, ui
   __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(base) + off, (lds_void_ptr)dst, 16, 0, 0);
 }
 
-// Issue the asynchronous global->LDS copies of one K and one V tile (block j).
-// Each wave instruction fills 64 consecutive 16-byte LDS units in row order.
-template <int D, int BS, int NW>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
-                                           int rows_in_mem, uint16_t* kdst, uint16_t* vdst, int wave, int lane,
-                                           const DmaPlan<D, BS, NW>& plan) {
-  using TP = TilePitch<D, BS>;
-  using PL = DmaPlan<D, BS, NW>;
-  if (rows_in_mem == BS) {  // uniform: a whole block, the planned offsets as they are
-#pragma unroll
-    for (int n = 0; n < PL::KN; ++n)
-      if (wave + NW * n < TP::KI) copy16_to_lds(kt, plan.k[n], kdst + (wave + NW * n) * 512);
-#pragma unroll
-    for (int n = 0; n < PL::VN; ++n)
-      if (wave + NW * n < TP::VI) copy16_to_lds(vt, plan.v[n], vdst + (wave + NW * n) * 512);
-    return;
-  }
-  // a planned offset row * D + col keeps its column; rows past the last valid
-  // one (only in a sequence's ragged last block) move to the last valid row
-  const uint32_t last = (uint32_t)(rows_in_mem - 1) * D * 2;
-#pragma unroll
-  for (int n = 0; n < PL::KN; ++n) {
-    const int i = wave + NW * n;
-    if (i < TP::KI) copy16_to_lds(kt, min(plan.k[n], last + (plan.k[n] & (2 * D - 1))), kdst + i * 512);
-  }
-#pragma unroll
-  for (int n = 0; n < PL::VN; ++n) {
-    const int i = wave + NW * n;
-    if (i < TP::VI) copy16_to_lds(vt, min(plan.v[n], last + (plan.v[n] & (2 * D - 1))), vdst + i * 512);
-  }
+// A buffer resource over one tile's rows in memory: `bytes` bounds it, and the
+// hardware's range check fills the copies of units at or past that bound (the
+// rows after a sequence's end, in its ragged last block) with zeros -- keys and
+// values that the masks already exclude -- at no per-lane cost.
+constexpr int kRawBufferWord3 = 0x00020000;  // word 3 of an untyped (raw) buffer resource
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, kRawBufferWord3);
 }
 
-// Issue the copies of one half of a tile: its keys (KEYS) or its values.
+// Issue the copies of one half of a tile -- its keys (KEYS) or its values -- of
+// which `rows_in_mem` rows lie in memory. Each wave instruction fills 64
+// consecutive 16-byte LDS units in row order; the first I / NW copies of every
+// wave always exist.
 template <int D, int BS, int NW, bool KEYS>
 __device__ __forceinline__ void issue_half(const uint16_t* __restrict__ src, int rows_in_mem, uint16_t* dst,
                                            int wave, const DmaPlan<D, BS, NW>& plan) {
@@ -191,13 +171,22 @@ __device__ __forceinline__ void issue_half(const uint16_t* __restrict__ src, int
   constexpr int N = KEYS ? PL::KN : PL::VN;
   constexpr int I = KEYS ? TP::KI : TP::VI;
   const uint32_t* off = KEYS ? plan.k : plan.v;
-  const bool whole = rows_in_mem == BS;  // uniform: a whole block takes the planned offsets as they are
-  const uint32_t last = (uint32_t)(rows_in_mem - 1) * D * 2;
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc(src, rows_in_mem * D * 2);
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     const int i = wave + NW * n;
-    if (i < I) copy16_to_lds(src, whole ? off[n] : min(off[n], last + (off[n] & (2 * D - 1))), dst + i * 512);
+    if (n < I / NW || i < I)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(dst + i * 512), 16, off[n], 0, 0, 0);
   }
+}
+
+// Issue the copies of one K and one V tile, keys first.
+template <int D, int BS, int NW>
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
+                                           int rows_in_mem, uint16_t* kdst, uint16_t* vdst, int wave,
+                                           const DmaPlan<D, BS, NW>& plan) {
+  issue_half<D, BS, NW, true>(kt, rows_in_mem, kdst, wave, plan);
+  issue_half<D, BS, NW, false>(vt, rows_in_mem, vdst, wave, plan);
 }
 
 // Wait until at most N of this wave's vector memory loads are outstanding.

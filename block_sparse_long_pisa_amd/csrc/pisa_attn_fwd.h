@@ -200,7 +200,7 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
   bool local;
   walk.at(0, sel, g, qb, local_rows, j, nvalid, local);
   issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
-                        wave, lane, plan);
+                        wave, plan);
   if constexpr (ST == 1) {
     // One stage, split by phase: the keys of tile t + 1 load while tile t's
     // softmax and value product run, its values while tile t + 1's scores run.
@@ -240,7 +240,7 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
     if (t + 1 < walk.ntiles) {
       walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
       issue_tile<D, BS, NW>(kbase + (int64_t)j1 * BS * D, vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K1,
-                            V1, wave, lane, plan);
+                            V1, wave, plan);
     }
     compute_tile<D, BS>(st, K0, V0, nvalid, local, j * BS, qpos, hi, c, wg_qmax);
     if (t + 1 >= walk.ntiles) break;
@@ -249,7 +249,7 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
     if (t + 2 < walk.ntiles) {
       walk.at(t + 2, sel, g, qb, local_rows, j, nvalid, local);
       issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
-                            wave, lane, plan);
+                            wave, plan);
     }
     compute_tile<D, BS>(st, K1, V1, nv1, loc1, j1 * BS, qpos, hi, c, wg_qmax);
   }
