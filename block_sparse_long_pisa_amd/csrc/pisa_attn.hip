@@ -42,10 +42,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2
                                                             float* __restrict__ lse, int parts, int order) {
   constexpr int NT = NW * 64;
   // kStages<NW> stages of K and V tiles, filled by asynchronous copies
-  __shared__ __attribute__((aligned(16))) uint16_t K0[TilePitch<D, BS>::KSIZE];
-  __shared__ __attribute__((aligned(16))) uint16_t V0[TilePitch<D, BS>::VSIZE];
-  __shared__ __attribute__((aligned(16))) uint16_t K1[kStages<NW> == 2 ? TilePitch<D, BS>::KSIZE : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t V1[kStages<NW> == 2 ? TilePitch<D, BS>::VSIZE : 8];
+  using TL = TilePitch<D, BS, kSwizzled<D, NW>>;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[TL::KSIZE];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[TL::VSIZE];
+  __shared__ __attribute__((aligned(16))) uint16_t K1[kStages<NW> == 2 ? TL::KSIZE : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t V1[kStages<NW> == 2 ? TL::VSIZE : 8];
   __shared__ int sel[kMaxTopK];
 
   // Persistent: each workgroup takes every gridDim.x-th (unit, part) item of its

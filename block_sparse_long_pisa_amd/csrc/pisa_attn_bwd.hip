@@ -37,7 +37,7 @@ enum : int { kFull = 0, kSinkPart = 1, kLocal = 2 };
 // the forward does. V is staged at the row pitch (dP^T = V dO^T). K is read both
 // as rows (S^T = K Q^T) and as columns (dQ^T += K^T dS^T), and no padded pitch
 // serves both without bank conflicts: at D = 128 its rows are unpadded 256-byte
-// rows with the logical 16-byte unit u of row r at u ^ dq_swz(r), for which the
+// rows with the logical 16-byte unit u of row r at u ^ tile_swz(r), for which the
 // bank-conflict counter of gfx950 reads zero on both reads; at D = 64 they are
 // padded to the transposing pitch.
 
@@ -47,8 +47,6 @@ struct DqKLayout {
   static constexpr int PITCH = kSwz ? D : TilePitch<D, BS>::V;  // elements per row
   static constexpr int SIZE = kSwz ? BS * D : TilePitch<D, BS>::VSIZE;
 };
-
-__device__ __forceinline__ int dq_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
 template <int D, int BS>
 struct DqState {
@@ -69,14 +67,14 @@ struct DqState {
 #pragma unroll
     for (int ds = 0; ds < D / 16; ++ds) {
       const int u = 2 * ds + hi;
-      offr[ds] = KL::kSwz ? (l32 * D + ((u ^ dq_swz(l32)) * 8)) * 2 : (l32 * KL::PITCH + u * 8) * 2;
+      offr[ds] = KL::kSwz ? (l32 * D + ((u ^ tile_swz(l32)) * 8)) * 2 : (l32 * KL::PITCH + u * 8) * 2;
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
       const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
       if (KL::kSwz) {
-        offtl[db] = (rr * D + (((col >> 3) ^ dq_swz(rr)) * 8) + (col & 7)) * 2;
-        offtu[db] = ((rr + 8) * D + (((col >> 3) ^ dq_swz(rr + 8)) * 8) + (col & 7)) * 2;
+        offtl[db] = (rr * D + (((col >> 3) ^ tile_swz(rr)) * 8) + (col & 7)) * 2;
+        offtu[db] = ((rr + 8) * D + (((col >> 3) ^ tile_swz(rr + 8)) * 8) + (col & 7)) * 2;
       } else {
         offtl[db] = (rr * KL::PITCH + col) * 2;
         offtu[db] = ((rr + 8) * KL::PITCH + col) * 2;
@@ -104,7 +102,7 @@ struct DqPlan {
       const int p = (wave + NW * n) * 64 + lane;
       if (KL::kSwz) {
         const int r = p / (D / 8);
-        k[n] = 2u * (r * D + (((p % (D / 8)) ^ dq_swz(r)) * 8));
+        k[n] = 2u * (r * D + (((p % (D / 8)) ^ tile_swz(r)) * 8));
       } else {
         k[n] = 2u * unit_src<D, TP::VU>(p, BS);
       }

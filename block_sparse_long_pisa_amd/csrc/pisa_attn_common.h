@@ -100,11 +100,16 @@ __device__ __forceinline__ TileWalk make_walk(const Geo& g, int qb, const int* s
 // consecutive rows at one 16-byte chunk land on distinct banks), V rows D + 32
 // apart (4 consecutive rows x 64 bytes, the transposing V^T reads, cover all
 // banks once). Every read is then a per-lane base register plus an immediate.
-template <int D, int BS = 128>
+// Swizzled tiles (SW, d = 128 only) are unpadded instead: 256-byte rows with the
+// logical 16-byte unit u of row r stored at u ^ tile_swz(r), which keeps both
+// patterns conflict-free with fewer bytes copied, at the price of a per-lane
+// offset per read step.
+template <int D, int BS = 128, bool SW = false>
 struct TilePitch {
-  static constexpr int K = D + 8;   // bf16 elements per K row
-  static constexpr int V = D + 32;  // bf16 elements per V row
-  static constexpr int KU = K / 8;  // 16-byte units per K row
+  static_assert(!SW || D == 128, "swizzled tiles have 256-byte rows");
+  static constexpr int K = SW ? D : D + 8;   // bf16 elements per K row
+  static constexpr int V = SW ? D : D + 32;  // bf16 elements per V row
+  static constexpr int KU = K / 8;           // 16-byte units per K row
   static constexpr int VU = V / 8;
   // whole 1 KB wave copies per tile; the LDS arrays are sized to match
   static constexpr int KI = (BS * KU + 63) / 64;
@@ -112,6 +117,12 @@ struct TilePitch {
   static constexpr int KSIZE = KI * 512;  // bf16 elements
   static constexpr int VSIZE = VI * 512;
 };
+
+// The unit swizzle of unpadded 256-byte rows: it depends on r mod 16 only. For
+// 16 rows read at one unit (row fragments) and for 8 rows read as 4 x 8-byte
+// pieces of a 32-byte slice (transposing reads) it spreads the reads over all
+// banks; the bank-conflict counter of gfx950 reads zero on both.
+__device__ __forceinline__ int tile_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
@@ -128,18 +139,29 @@ __device__ __forceinline__ int unit_src(int u, int rows) {
 
 // Per-lane source offsets, in bytes, of this wave's copies of a full tile
 // (they do not change from tile to tile).
-template <int D, int BS, int NW>
+template <int D_, int BS_, int NW_, bool SW_ = false>
 struct DmaPlan {
-  using TP = TilePitch<D, BS>;
+  static constexpr int D = D_, BS = BS_, NW = NW_;
+  using TP = TilePitch<D, BS, SW_>;
   static constexpr int KN = (TP::KI + NW - 1) / NW;
   static constexpr int VN = (TP::VI + NW - 1) / NW;
   uint32_t k[KN];
   uint32_t v[VN];
+  // source element offset of the physical unit p of a tile with UPR units per row
+  template <int UPR>
+  static __device__ __forceinline__ int src(int p) {
+    if constexpr (SW_) {
+      const int r = p / UPR;
+      return r * D + ((p % UPR) ^ tile_swz(r)) * 8;
+    } else {
+      return unit_src<D, UPR>(p, BS);
+    }
+  }
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int n = 0; n < KN; ++n) k[n] = 2u * unit_src<D, TP::KU>((wave + NW * n) * 64 + lane, BS);
+    for (int n = 0; n < KN; ++n) k[n] = 2u * src<TP::KU>((wave + NW * n) * 64 + lane);
 #pragma unroll
-    for (int n = 0; n < VN; ++n) v[n] = 2u * unit_src<D, TP::VU>((wave + NW * n) * 64 + lane, BS);
+    for (int n = 0; n < VN; ++n) v[n] = 2u * src<TP::VU>((wave + NW * n) * 64 + lane);
   }
 };
 
@@ -163,15 +185,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
 // which `rows_in_mem` rows lie in memory. Each wave instruction fills 64
 // consecutive 16-byte LDS units in row order; the first I / NW copies of every
 // wave always exist.
-template <int D, int BS, int NW, bool KEYS>
+template <bool KEYS, typename Plan>
 __device__ __forceinline__ void issue_half(const uint16_t* __restrict__ src, int rows_in_mem, uint16_t* dst,
-                                           int wave, const DmaPlan<D, BS, NW>& plan) {
-  using TP = TilePitch<D, BS>;
-  using PL = DmaPlan<D, BS, NW>;
-  constexpr int N = KEYS ? PL::KN : PL::VN;
+                                           int wave, const Plan& plan) {
+  using TP = typename Plan::TP;
+  constexpr int NW = Plan::NW;
+  constexpr int N = KEYS ? Plan::KN : Plan::VN;
   constexpr int I = KEYS ? TP::KI : TP::VI;
   const uint32_t* off = KEYS ? plan.k : plan.v;
-  const __amdgpu_buffer_rsrc_t r = tile_rsrc(src, rows_in_mem * D * 2);
+  const __amdgpu_buffer_rsrc_t r = tile_rsrc(src, rows_in_mem * Plan::D * 2);
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     const int i = wave + NW * n;
@@ -181,12 +203,12 @@ __device__ __forceinline__ void issue_half(const uint16_t* __restrict__ src, int
 }
 
 // Issue the copies of one K and one V tile, keys first.
-template <int D, int BS, int NW>
+template <typename Plan>
 __device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
                                            int rows_in_mem, uint16_t* kdst, uint16_t* vdst, int wave,
-                                           const DmaPlan<D, BS, NW>& plan) {
-  issue_half<D, BS, NW, true>(kt, rows_in_mem, kdst, wave, plan);
-  issue_half<D, BS, NW, false>(vt, rows_in_mem, vdst, wave, plan);
+                                           const Plan& plan) {
+  issue_half<true>(kt, rows_in_mem, kdst, wave, plan);
+  issue_half<false>(vt, rows_in_mem, vdst, wave, plan);
 }
 
 // Wait until at most N of this wave's vector memory loads are outstanding.

@@ -10,16 +10,48 @@
 namespace pisa {
 namespace {
 
-template <int D, int BS>
+// Units of at most two waves take swizzled (unpadded) tiles at d = 128: their
+// kernel is bound by the copies' traffic, and the per-lane offset tables fit in
+// their registers.
+template <int D, int NW>
+constexpr bool kSwizzled = D == 128 && NW <= 2;
+
+template <int D, int BS, bool SW>
 struct AttnState {
-  static constexpr int NKB = BS / 32;
+  using TP = TilePitch<D, BS, SW>;
   static constexpr int NDS = D / 16;
   static constexpr int NDB = D / 32;
   bf16x8_t qf[NDS];
   f32x16_t oacc[NDB];
   float m_run, l_run;
-  int offk;      // byte offset of this lane's first K-fragment chunk in a K tile
-  int offv;      // byte offset of this lane's first V^T transposing read in a V tile
+  // byte offsets in a tile of this lane's K-fragment reads (one per step ds when
+  // swizzled, else the first) and of its V^T transposing reads (one per slice db
+  // and half of the 16-row step when swizzled, else the first)
+  int offk[SW ? NDS : 1];
+  int offv[SW ? NDB : 1];
+  int offu[SW ? NDB : 1];
+  __device__ __forceinline__ int k_at(int ds) const { return SW ? offk[ds] : offk[0] + ds * 32; }
+  __device__ __forceinline__ int v_lo(int db) const { return SW ? offv[db] : offv[0] + db * 64; }
+  __device__ __forceinline__ int v_up(int db) const { return SW ? offu[db] : offv[0] + db * 64 + 8 * TP::V * 2; }
+  __device__ __forceinline__ void init_offsets(int lane) {
+    const int l32 = lane & 31, hi = lane >> 5;
+    // K fragment: row l32, d = ds*16 + hi*8. V^T transposing read: lanes 4j..4j+3
+    // of each 16-lane block supply row j's four 8-byte pieces of a 16-column slice.
+    const int rr = hi * 4 + ((lane & 15) >> 2);
+    if constexpr (SW) {
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) offk[ds] = (l32 * D + (((2 * ds + hi) ^ tile_swz(l32)) * 8)) * 2;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        offv[db] = (rr * D + (((col >> 3) ^ tile_swz(rr)) * 8) + (col & 7)) * 2;
+        offu[db] = ((rr + 8) * D + (((col >> 3) ^ tile_swz(rr + 8)) * 8) + (col & 7)) * 2;
+      }
+    } else {
+      offk[0] = (l32 * TP::K + hi * 8) * 2;
+      offv[0] = (rr * TP::V + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+    }
+  }
 };
 
 // Keys per chunk of a tile: the scores of at most 64 keys (32 live accumulator
@@ -30,8 +62,8 @@ constexpr int kChunk = BS < 64 ? BS : 64;
 // S^T = K Q^T for the keys [ch * KC, ch * KC + KC) of the tile in `ks`, with the
 // keys beyond `nvalid` (partial block) and after the query (causal diagonal)
 // masked.
-template <int D, int BS>
-__device__ __forceinline__ void tile_scores(const AttnState<D, BS>& st, const uint16_t* ks, int ch, int nvalid,
+template <int D, int BS, bool SW>
+__device__ __forceinline__ void tile_scores(const AttnState<D, BS, SW>& st, const uint16_t* ks, int ch, int nvalid,
                                             bool local, int key0, int qpos, int hi,
                                             f32x16_t (&sacc)[kChunk<BS> / 32]) {
   constexpr int NDS = D / 16;
@@ -44,8 +76,8 @@ __device__ __forceinline__ void tile_scores(const AttnState<D, BS>& st, const ui
     for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb_base + st.offk + ds * 32 +
-                                                            (ch * KC + kb * 32) * TilePitch<D>::K * 2);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb_base + st.k_at(ds) +
+                                                            (ch * KC + kb * 32) * TilePitch<D, BS, SW>::K * 2);
       sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[ds], sacc[kb], 0, 0, 0);
     }
   }
@@ -62,8 +94,8 @@ __device__ __forceinline__ void tile_scores(const AttnState<D, BS>& st, const ui
 
 // Online softmax of one chunk's scores and O^T += V^T P^T with the chunk's
 // values from the tile in `vs`.
-template <int D, int BS>
-__device__ __forceinline__ void tile_update(AttnState<D, BS>& st, f32x16_t (&sacc)[kChunk<BS> / 32],
+template <int D, int BS, bool SW>
+__device__ __forceinline__ void tile_update(AttnState<D, BS, SW>& st, f32x16_t (&sacc)[kChunk<BS> / 32],
                                             const uint16_t* vs, int ch, float c) {
   constexpr int NDB = D / 32;
   constexpr int KC = kChunk<BS>;
@@ -108,13 +140,11 @@ __device__ __forceinline__ void tile_update(AttnState<D, BS>& st, f32x16_t (&sac
       bf16x8_t pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][hh * 8 + e];
-      const int step = (ch * KC + kb * 32 + hh * 16) * TilePitch<D>::V * 2;
+      const int step = (ch * KC + kb * 32 + hh * 16) * TilePitch<D, BS, SW>::V * 2;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_ptr)(vb_base + st.offv + step + db * 64));
-        const v4i16_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_v4i16_ptr)(vb_base + st.offv + step + db * 64 + 8 * TilePitch<D>::V * 2));
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vb_base + st.v_lo(db) + step));
+        const v4i16_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vb_base + st.v_up(db) + step));
         const v4i16_t a8[2] = {lo, up};
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a8);
         st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, st.oacc[db], 0, 0, 0);
@@ -125,8 +155,8 @@ __device__ __forceinline__ void tile_update(AttnState<D, BS>& st, f32x16_t (&sac
 }
 
 // One key tile: S^T = K Q^T, mask, online softmax, O^T += V^T P^T, chunk by chunk.
-template <int D, int BS>
-__device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_t* ks, const uint16_t* vs, int nvalid,
+template <int D, int BS, bool SW>
+__device__ __forceinline__ void compute_tile(AttnState<D, BS, SW>& st, const uint16_t* ks, const uint16_t* vs, int nvalid,
                                              bool local, int key0, int qpos, int hi, float c, int wg_qmax) {
   constexpr int KC = kChunk<BS>;
 #pragma unroll
@@ -135,8 +165,8 @@ __device__ __forceinline__ void compute_tile(AttnState<D, BS>& st, const uint16_
     // the causal diagonal, contributes nothing to any row (uniform test)
     if (ch > 0 && (ch * KC >= nvalid || (local && key0 + ch * KC > wg_qmax))) break;
     f32x16_t sacc[KC / 32];
-    tile_scores<D, BS>(st, ks, ch, nvalid, local, key0, qpos, hi, sacc);
-    tile_update<D, BS>(st, sacc, vs, ch, c);
+    tile_scores(st, ks, ch, nvalid, local, key0, qpos, hi, sacc);
+    tile_update(st, sacc, vs, ch, c);
   }
 }
 
@@ -166,7 +196,8 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
   const bool qvalid = qpos < g.N;
   const int local_rows = min(BS, g.N - qb * BS);
 
-  AttnState<D, BS> st;
+  constexpr bool SW = kSwizzled<D, NW>;
+  AttnState<D, BS, SW> st;
   {
     const uint16_t* qrow = q + (((int64_t)b * g.Hq + h) * g.N + (qvalid ? qpos : 0)) * D;
 #pragma unroll
@@ -181,10 +212,7 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
     for (int i = 0; i < 16; ++i) st.oacc[db][i] = 0.f;
   st.m_run = -__builtin_inff();
   st.l_run = 0.f;
-  // K fragment: row l32, d = ds*16 + hi*8. V^T transposing read: lanes 4j..4j+3 of
-  // each 16-lane block supply row j's four 8-byte pieces of a 16-column slice.
-  st.offk = (l32 * TilePitch<D>::K + hi * 8) * 2;
-  st.offv = ((hi * 4 + ((lane & 15) >> 2)) * TilePitch<D>::V + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+  st.init_offsets(lane);
   const float c = g.scale * kLog2e;
   // last query position any wave of this workgroup holds (chunks of keys beyond
   // it are masked for every row and are skipped)
@@ -193,13 +221,13 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
   const uint16_t* kbase = k + ((int64_t)b * g.Hkv + kvh) * g.N * D;
   const uint16_t* vbase = v + ((int64_t)b * g.Hkv + kvh) * g.N * D;
   const TileWalk walk = make_walk(g, qb, sel, nsel);
-  DmaPlan<D, BS, NW> plan;
+  DmaPlan<D, BS, NW, SW> plan;
   plan.init(wave, lane);
 
   int j, nvalid;
   bool local;
   walk.at(0, sel, g, qb, local_rows, j, nvalid, local);
-  issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
+  issue_tile(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
                         wave, plan);
   if constexpr (ST == 1) {
     // One stage, split by phase: the keys of tile t + 1 load while tile t's
@@ -208,12 +236,12 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
     // until at most VMIN of its copies are outstanding -- fewer than the V
     // copies it issued after them -- means its K copies have landed.
     static_assert(BS <= 64, "a one-stage tile is one chunk of keys");
-    constexpr int VMIN = TilePitch<D, BS>::VI / NW;
+    constexpr int VMIN = TilePitch<D, BS, SW>::VI / NW;
     for (int t = 0; t < walk.ntiles; ++t) {
       wait_loads<VMIN>();
       __syncthreads();  // K(t) has landed for every wave
       f32x16_t sacc[BS / 32];
-      tile_scores<D, BS>(st, K0, 0, nvalid, local, j * BS, qpos, hi, sacc);
+      tile_scores(st, K0, 0, nvalid, local, j * BS, qpos, hi, sacc);
       wait_loads<0>();
       __syncthreads();  // V(t) has landed; every wave is done with K(t)
       const bool more = t + 1 < walk.ntiles;
@@ -221,12 +249,12 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
       bool loc1 = false;
       if (more) {
         walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
-        issue_half<D, BS, NW, true>(kbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K0, wave, plan);
+        issue_half<true>(kbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K0, wave, plan);
       }
-      tile_update<D, BS>(st, sacc, V0, 0, c);
+      tile_update(st, sacc, V0, 0, c);
       if (!more) break;
       lds_read_barrier();  // every wave is done with V(t); K(t + 1) keeps loading
-      issue_half<D, BS, NW, false>(vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), V0, wave, plan);
+      issue_half<false>(vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), V0, wave, plan);
       j = j1;
       nvalid = nv1;
       local = loc1;
@@ -239,19 +267,19 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
     bool loc1 = false;
     if (t + 1 < walk.ntiles) {
       walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
-      issue_tile<D, BS, NW>(kbase + (int64_t)j1 * BS * D, vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K1,
+      issue_tile(kbase + (int64_t)j1 * BS * D, vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K1,
                             V1, wave, plan);
     }
-    compute_tile<D, BS>(st, K0, V0, nvalid, local, j * BS, qpos, hi, c, wg_qmax);
+    compute_tile(st, K0, V0, nvalid, local, j * BS, qpos, hi, c, wg_qmax);
     if (t + 1 >= walk.ntiles) break;
     // odd tile: compute from stage 1 while stage 0 fills
     wait_loads_and_sync();
     if (t + 2 < walk.ntiles) {
       walk.at(t + 2, sel, g, qb, local_rows, j, nvalid, local);
-      issue_tile<D, BS, NW>(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
+      issue_tile(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
                             wave, plan);
     }
-    compute_tile<D, BS>(st, K1, V1, nv1, loc1, j1 * BS, qpos, hi, c, wg_qmax);
+    compute_tile(st, K1, V1, nv1, loc1, j1 * BS, qpos, hi, c, wg_qmax);
   }
 
   if (qvalid) {

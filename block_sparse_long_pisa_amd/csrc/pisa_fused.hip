@@ -87,7 +87,7 @@ __global__ __launch_bounds__(NW * 64) void select_attn_bf16_kernel(Geo g, const 
                                                                    uint16_t* __restrict__ out,
                                                                    float* __restrict__ lse, int parts) {
   constexpr int NT = NW * 64;
-  using TP = TilePitch<D, BS>;
+  using TP = TilePitch<D, BS, kSwizzled<D, NW>>;
   // two stages of K and V tiles; before the first tile they hold the mean's and
   // the descent's scratch
   __shared__ __attribute__((aligned(16))) uint16_t stage[2 * (TP::KSIZE + TP::VSIZE)];
