@@ -35,8 +35,8 @@ BF16_PEAK = 2.5e15  # flop/s, dense bf16 matrix cores
 COPY_SCALE = {"fetch": 1048576.0 / 524337.8, "write": 1048576.0 / 1048576.0}
 MEASURED_TRAFFIC = {
     # step: (sources, sha256 prefix of their bytes in this order, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "1cd2b5dfd169d830",
-                  5953631.6, 1048576.2),
+    "attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "d6599a8cfabbf7b3",
+                  5965864.2, 1048576.5),
     "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "1992710658b9dd0f",
                 131119.6 + 337.6, 4608.2 + 72.0),  # leaf and levels 1, then levels 2 and up
     "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "5d34d5121909d47d",
