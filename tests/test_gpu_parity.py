@@ -30,6 +30,8 @@ SMALL = {
     "tiny_f32_n1024": (gen.WORKLOADS[1]["problem"], "every_block", 1.0),
     "gqa_ragged": (P(2, 8, 2, 4000, 128, 128, 4, 3, 4, 64, "bf16"), ("uniform_pairs", 4), None),
     "mha_bs64_ragged": (P(1, 4, 4, 3000, 128, 64, 8, 2, 6, 64, "bf16"), ("uniform_pairs", 4), None),
+    # one-wave units (32 query rows) of d = 128: swizzled tiles, one split-phase stage
+    "mha_bs32_ragged": (P(1, 2, 2, 1000, 128, 32, 4, 3, 4, 64, "bf16"), ("uniform_pairs", 4), None),
     "d64_partial_sink": (P(1, 4, 1, 2065, 64, 32, 4, 3, 3, 40, "bf16"), ("uniform_pairs", 4), None),
     "fp32_d128": (P(1, 2, 1, 700, 128, 64, 2, 3, 2, 0, "f32"), ("uniform_pairs", 2), 1.0),
     "group8": (P(1, 16, 2, 2048, 128, 128, 4, 2, 3, 64, "bf16"), ("uniform_pairs", 4), None),
