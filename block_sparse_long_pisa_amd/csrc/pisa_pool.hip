@@ -239,27 +239,27 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
   }
 }
 
-// All levels from 2 up in one launch: a workgroup owns one top-level node and
-// builds its subtree level by level from the level-1 summaries. Within a level
-// each thread folds NM nodes of one column, and all F x NM child loads of a
-// round are issued before any is used. 1024 threads: a subtree of up to
-// 8 * 64 / F level-2 nodes (d = 128) takes a single round of loads, so even a
-// slab whose top level holds two nodes builds in a few dependent steps.
+// Levels lo..top (lo >= 2) in one launch: a workgroup owns one node of level
+// `top` and builds its subtree level by level from the level-(lo - 1)
+// summaries. Within a level each thread folds NM nodes of one column, and all
+// F x NM child loads of a round are issued before any is used. 1024 threads: a
+// subtree of up to 8 * 64 / F level-lo nodes (d = 128) takes a single round of
+// loads.
 constexpr int kUpperThreads = 1024;
 
 template <int D, bool MX, int F>
-__global__ __launch_bounds__(kUpperThreads) void pool_upper_kernel(Geo g, float* __restrict__ pyr) {
+__global__ __launch_bounds__(kUpperThreads) void pool_upper_kernel(Geo g, float* __restrict__ pyr, int lo, int top) {
   using PO = Pool<MX>;
   constexpr int CPT = kUpperThreads / D;  // node groups per column
   constexpr int NM = F >= 4 ? 64 / F : 16;  // nodes a thread folds per round
-  const int top = blockIdx.x;
+  const int root = blockIdx.x;
   const int slab = blockIdx.y;
   float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
   const int c = threadIdx.x % D;
   const int grp = threadIdx.x / D;
-  for (int l = 2; l < g.L; ++l) {
-    const int sub = g.span[g.L - 1] / g.span[l];  // level-l nodes under one top node
-    const int n0 = top * sub;
+  for (int l = lo; l <= top; ++l) {
+    const int sub = g.span[top] / g.span[l];  // level-l nodes under one level-top node
+    const int n0 = root * sub;
     const int n1 = min(n0 + sub, g.nodes[l]);
     const int below = g.nodes[l - 1];
     for (int nb0 = n0 + grp * NM; nb0 < n1; nb0 += CPT * NM) {
@@ -283,16 +283,33 @@ __global__ __launch_bounds__(kUpperThreads) void pool_upper_kernel(Geo g, float*
   }
 }
 
+template <int D, bool MX, int F>
+hipError_t launch_upper_f(const Geo& g, float* pyr, int lo, int top, hipStream_t s) {
+  const dim3 grid(g.nodes[top], g.B * g.Hkv);
+  hipLaunchKernelGGL((pool_upper_kernel<D, MX, F>), grid, dim3(kUpperThreads), 0, s, g, pyr, lo, top);
+  return hipGetLastError();
+}
+
+// Levels 2 and up. With five levels or more the levels below the top go first,
+// one workgroup per node of the level under the top (the top level alone would
+// leave a slab as few workgroups as it has top nodes, each folding a long chain
+// of levels), then the top level in a second launch.
+template <int D, bool MX, int F>
+hipError_t launch_upper_levels(const Geo& g, float* pyr, hipStream_t s) {
+  if (g.L < 5) return launch_upper_f<D, MX, F>(g, pyr, 2, g.L - 1, s);
+  const hipError_t e = launch_upper_f<D, MX, F>(g, pyr, 2, g.L - 2, s);
+  if (e != hipSuccess) return e;
+  return launch_upper_f<D, MX, F>(g, pyr, g.L - 1, g.L - 1, s);
+}
+
 template <int D, bool MX>
 hipError_t launch_upper(const Geo& g, float* pyr, hipStream_t s) {
-  const dim3 grid(g.nodes[g.L - 1], g.B * g.Hkv);
   switch (g.f) {
-    case 2: hipLaunchKernelGGL((pool_upper_kernel<D, MX, 2>), grid, dim3(kUpperThreads), 0, s, g, pyr); break;
-    case 4: hipLaunchKernelGGL((pool_upper_kernel<D, MX, 4>), grid, dim3(kUpperThreads), 0, s, g, pyr); break;
-    case 8: hipLaunchKernelGGL((pool_upper_kernel<D, MX, 8>), grid, dim3(kUpperThreads), 0, s, g, pyr); break;
-    default: hipLaunchKernelGGL((pool_upper_kernel<D, MX, 16>), grid, dim3(kUpperThreads), 0, s, g, pyr); break;
+    case 2: return launch_upper_levels<D, MX, 2>(g, pyr, s);
+    case 4: return launch_upper_levels<D, MX, 4>(g, pyr, s);
+    case 8: return launch_upper_levels<D, MX, 8>(g, pyr, s);
+    default: return launch_upper_levels<D, MX, 16>(g, pyr, s);
   }
-  return hipGetLastError();
 }
 
 template <typename T, int D, bool MX>
