@@ -243,15 +243,18 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
 // `top` and builds its subtree level by level from the level-(lo - 1)
 // summaries. Within a level each thread folds NM nodes of one column, and all
 // F x NM child loads of a round are issued before any is used. 1024 threads: a
-// subtree of up to 8 * 64 / F level-lo nodes (d = 128) takes a single round of
-// loads.
+// subtree of up to 8 * NM level-lo nodes (d = 128) takes a single round of
+// loads; NM = 64 / F for large subtrees, 1 when the subtree's level lo has at
+// most 8 nodes (then every node gets its own threads).
 constexpr int kUpperThreads = 1024;
 
-template <int D, bool MX, int F>
+template <int F>
+constexpr int kUpperNodes = F >= 4 ? 64 / F : 16;
+
+template <int D, bool MX, int F, int NM>
 __global__ __launch_bounds__(kUpperThreads) void pool_upper_kernel(Geo g, float* __restrict__ pyr, int lo, int top) {
   using PO = Pool<MX>;
   constexpr int CPT = kUpperThreads / D;  // node groups per column
-  constexpr int NM = F >= 4 ? 64 / F : 16;  // nodes a thread folds per round
   const int root = blockIdx.x;
   const int slab = blockIdx.y;
   float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
@@ -286,7 +289,11 @@ __global__ __launch_bounds__(kUpperThreads) void pool_upper_kernel(Geo g, float*
 template <int D, bool MX, int F>
 hipError_t launch_upper_f(const Geo& g, float* pyr, int lo, int top, hipStream_t s) {
   const dim3 grid(g.nodes[top], g.B * g.Hkv);
-  hipLaunchKernelGGL((pool_upper_kernel<D, MX, F>), grid, dim3(kUpperThreads), 0, s, g, pyr, lo, top);
+  if (g.span[top] / g.span[lo] <= kUpperThreads / D)
+    hipLaunchKernelGGL((pool_upper_kernel<D, MX, F, 1>), grid, dim3(kUpperThreads), 0, s, g, pyr, lo, top);
+  else
+    hipLaunchKernelGGL((pool_upper_kernel<D, MX, F, kUpperNodes<F>>), grid, dim3(kUpperThreads), 0, s, g, pyr, lo,
+                       top);
   return hipGetLastError();
 }
 
