@@ -32,6 +32,10 @@ SMALL = {
     "mha_bs64_ragged": (P(1, 4, 4, 3000, 128, 64, 8, 2, 6, 64, "bf16"), ("uniform_pairs", 4), None),
     # one-wave units (32 query rows) of d = 128: swizzled tiles, one split-phase stage
     "mha_bs32_ragged": (P(1, 2, 2, 1000, 128, 32, 4, 3, 4, 64, "bf16"), ("uniform_pairs", 4), None),
+    # slab counts that divide among the 8 XCDs: the attention's XCD-partitioned item
+    # order, with two-wave (8 slabs) and eight-wave (16 slabs, two parts) units
+    "xcd_order_mha8": (P(1, 8, 8, 1000, 128, 64, 4, 2, 4, 64, "bf16"), ("uniform_pairs", 4), None),
+    "xcd_order_gqa16": (P(2, 32, 8, 1500, 128, 128, 4, 2, 4, 64, "bf16"), ("uniform_pairs", 4), None),
     "d64_partial_sink": (P(1, 4, 1, 2065, 64, 32, 4, 3, 3, 40, "bf16"), ("uniform_pairs", 4), None),
     "fp32_d128": (P(1, 2, 1, 700, 128, 64, 2, 3, 2, 0, "f32"), ("uniform_pairs", 2), 1.0),
     "group8": (P(1, 16, 2, 2048, 128, 128, 4, 2, 3, 64, "bf16"), ("uniform_pairs", 4), None),
