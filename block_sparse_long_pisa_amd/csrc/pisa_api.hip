@@ -308,15 +308,17 @@ pisa_status pisa_decode_step_ragged_noalloc(const pisa_problem* p, const void* q
   if (g.B == 0) return ok();
   if (cache_lens == nullptr) return fail(PISA_ERR_NULL, "cache_lens is NULL");
   if (((uintptr_t)cache_lens & 3u) != 0) return fail(PISA_ERR_ALIGN, "cache_lens must be 4-byte aligned");
-  const size_t need = pisa::decode_workspace_bytes(g);
-  if (need > pisa::kDecodeScratchBytes)
-    return fail(PISA_ERR_WORKSPACE, "this problem needs a %zu-byte decode workspace; the static one holds %zu bytes",
-                need, pisa::kDecodeScratchBytes);
   void* ws = nullptr;
   hipError_t e = pisa::decode_scratch_ptr(&ws);
   if (e != hipSuccess) return hip_fail(e, "pisa_decode_step_ragged_noalloc scratch lookup");
-  s = check_decode(g, q, k_cache, v_cache, pyramid, out, ws, pisa::kDecodeScratchBytes);
+  // the problem and its buffers first (against the workspace it would need),
+  // then whether that workspace fits the static one
+  const size_t need = pisa::decode_workspace_bytes(g);
+  s = check_decode(g, q, k_cache, v_cache, pyramid, out, ws, need);
   if (s != PISA_OK) return s;
+  if (need > pisa::kDecodeScratchBytes)
+    return fail(PISA_ERR_WORKSPACE, "this problem needs a %zu-byte decode workspace; the static one holds %zu bytes",
+                need, pisa::kDecodeScratchBytes);
   e = pisa::launch_decode(g, q, k_cache, v_cache, pyramid, cache_lens, 0, out, lse, idx_out, cnt_out, ws, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "pisa_decode_step_ragged_noalloc launch");
 }
