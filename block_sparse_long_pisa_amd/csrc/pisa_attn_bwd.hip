@@ -111,27 +111,28 @@ struct DqPlan {
 };
 
 // Issue the copies of one dQ stage: V tile vt into vdst (row pitch), K tile kt
-// into kdst (DqKLayout). Rows past `rows_in_mem` re-read the last valid row.
+// into kdst (DqKLayout), through buffer resources bounded by the `rows_in_mem`
+// rows in memory: the rows past a sequence's end come in as zeros (their keys
+// are masked).
 template <int D, int BS, int NW>
 __device__ __forceinline__ void issue_dq_tile(const uint16_t* __restrict__ vt, const uint16_t* __restrict__ kt,
-                                              int rows_in_mem, uint16_t* vdst, uint16_t* kdst, int wave, int lane,
+                                              int rows_in_mem, uint16_t* vdst, uint16_t* kdst, int wave,
                                               const DqPlan<D, BS, NW>& plan) {
   using PL = DqPlan<D, BS, NW>;
-  // a whole block takes the planned offsets as they are (uniform test); in a
-  // ragged last block, rows past the last valid one move to it
-  const bool whole = rows_in_mem == BS;
-  const uint32_t last = (uint32_t)(rows_in_mem - 1) * D * 2;
+  constexpr int VI = TilePitch<D, BS>::KI;
+  const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vt, rows_in_mem * D * 2);
+  const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kt, rows_in_mem * D * 2);
 #pragma unroll
   for (int n = 0; n < PL::VN; ++n) {
     const int i = wave + NW * n;
-    if (i < TilePitch<D, BS>::KI)
-      copy16_to_lds(vt, whole ? plan.v[n] : min(plan.v[n], last + (plan.v[n] & (2 * D - 1))), vdst + i * 512);
+    if (n < VI / NW || i < VI)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_ptr)(vdst + i * 512), 16, plan.v[n], 0, 0, 0);
   }
 #pragma unroll
   for (int n = 0; n < PL::KN; ++n) {
     const int i = wave + NW * n;
-    if (i < PL::KCOP)
-      copy16_to_lds(kt, whole ? plan.k[n] : min(plan.k[n], last + (plan.k[n] & (2 * D - 1))), kdst + i * 512);
+    if (n < PL::KCOP / NW || i < PL::KCOP)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_ptr)(kdst + i * 512), 16, plan.k[n], 0, 0, 0);
   }
 }
 
@@ -279,7 +280,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(Geo g, const uint16_t* 
   bool local;
   walk.at(0, sel, g, qb, local_rows, j, nvalid, local);
   issue_dq_tile<D, BS, NW>(vbase + (int64_t)j * BS * D, kbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), VS0, KS0,
-                           wave, lane, plan);
+                           wave, plan);
   for (int t = 0; t < walk.ntiles; t += 2) {
     wait_loads_and_sync();
     int j1 = 0, nv1 = 0;
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(Geo g, const uint16_t* 
     if (t + 1 < walk.ntiles) {
       walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
       issue_dq_tile<D, BS, NW>(vbase + (int64_t)j1 * BS * D, kbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS),
-                               VS1, KS1, wave, lane, plan);
+                               VS1, KS1, wave, plan);
     }
     dq_tile<D, BS>(st, KS0, VS0, nvalid, local, j * BS, qpos, l32, hi, c, wg_qmax);
     if (t + 1 >= walk.ntiles) break;
@@ -295,7 +296,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(Geo g, const uint16_t* 
     if (t + 2 < walk.ntiles) {
       walk.at(t + 2, sel, g, qb, local_rows, j, nvalid, local);
       issue_dq_tile<D, BS, NW>(vbase + (int64_t)j * BS * D, kbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), VS0,
-                               KS0, wave, lane, plan);
+                               KS0, wave, plan);
     }
     dq_tile<D, BS>(st, KS1, VS1, nv1, loc1, j1 * BS, qpos, l32, hi, c, wg_qmax);
   }
@@ -467,8 +468,10 @@ struct KvPlan {
 };
 
 // Issue the copies of one (query block, head) stage: Q and dO rows (swizzled),
-// and the rows' lse2 and D (64 floats per wave instruction). Rows past the
-// sequence re-read the last row; they are masked by `rows`.
+// and the rows' lse2 and D (64 floats per wave instruction). Q and dO come
+// through buffer resources bounded by the rows in memory, so rows past the
+// sequence arrive as zeros; their lse2 and D re-read the last row's. Those
+// rows are masked by `rows`.
 template <int D, int BS, int NW>
 __device__ __forceinline__ void issue_kv_rows(const Geo& g, const uint16_t* q, const uint16_t* dout,
                                               const float* lse2, const float* rowdot, int b, int h, int qb,
@@ -477,16 +480,13 @@ __device__ __forceinline__ void issue_kv_rows(const Geo& g, const uint16_t* q, c
   using PL = KvPlan<D, BS, NW>;
   const int64_t r0 = ((int64_t)b * g.Hq + h) * g.N + (int64_t)qb * BS;
   const int rows = min(BS, g.N - qb * BS);
-  const uint32_t last = (uint32_t)(rows - 1) * D * 2;
-  const bool whole = rows == BS;  // uniform: the planned offsets as they are
-  const uint16_t* qt = q + r0 * D;
-  const uint16_t* ot = dout + r0 * D;
+  const __amdgpu_buffer_rsrc_t rq = tile_rsrc(q + r0 * D, rows * D * 2);
+  const __amdgpu_buffer_rsrc_t ro = tile_rsrc(dout + r0 * D, rows * D * 2);
 #pragma unroll
   for (int n = 0; n < PL::NC; ++n) {
-    const uint32_t off = whole ? plan.src[n] : min(plan.src[n], last + (plan.src[n] & (2 * D - 1)));
     const int i = wave + NW * n;
-    copy16_to_lds(qt, off, qdst + i * 512);
-    copy16_to_lds(ot, off, odst + i * 512);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_ptr)(qdst + i * 512), 16, plan.src[n], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ro, (lds_void_ptr)(odst + i * 512), 16, plan.src[n], 0, 0, 0);
   }
 #pragma unroll
   for (int n = 0; n < (BS + 63) / 64; ++n) {

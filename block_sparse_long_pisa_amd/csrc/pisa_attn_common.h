@@ -165,17 +165,12 @@ struct DmaPlan {
   }
 };
 
-// One 16-byte copy per lane from a wave-uniform base plus this lane's 32-bit
-// byte offset: the address form whose base sits in scalar registers, so that a
-// copy costs no per-lane 64-bit address arithmetic.
-__device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, uint16_t* dst) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(base) + off, (lds_void_ptr)dst, 16, 0, 0);
-}
-
 // A buffer resource over one tile's rows in memory: `bytes` bounds it, and the
 // hardware's range check fills the copies of units at or past that bound (the
-// rows after a sequence's end, in its ragged last block) with zeros -- keys and
-// values that the masks already exclude -- at no per-lane cost.
+// rows after a sequence's end, in its ragged last block) with zeros -- rows that
+// the masks already exclude -- at no per-lane cost. A copy is then one 16-byte
+// load per lane from the resource's scalar base plus this lane's 32-bit byte
+// offset, with no per-lane 64-bit address arithmetic.
 constexpr int kRawBufferWord3 = 0x00020000;  // word 3 of an untyped (raw) buffer resource
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, kRawBufferWord3);
