@@ -3,7 +3,8 @@
 Inputs are drawn on the GPU (gen.device_inputs) and copied to the host for the
 oracle. Every pyramid summary and every selection is compared; attention
 outputs are compared on sampled query blocks (the planted ones, the first and
-last blocks and a seeded random sample), decode on sampled sequences.
+last blocks, a seeded random sample and several hundred units spread evenly over
+all of them), decode on sampled sequences.
 """
 
 import math
@@ -20,7 +21,11 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-def _sample_units(p, man, n_random=12, seed=0):
+def _sample_units(p, man, n_random=12, seed=0, n_spread=0):
+    """Planted units, the first and last blocks, a seeded random sample, and
+    n_spread units evenly spaced over all (batch, kv head, query block) units --
+    over every slab and block position, and so over the attention's persistent
+    workgroups and their item orders."""
     rng = np.random.default_rng(seed)
     units = set()
     for n in man["needles"][:12]:
@@ -30,7 +35,17 @@ def _sample_units(p, man, n_random=12, seed=0):
         units.update({(0, g, 0), (0, g, 1), (0, g, nb - 1)})
     for _ in range(n_random):
         units.add((int(rng.integers(p.batch)), int(rng.integers(p.heads_kv)), int(rng.integers(nb))))
+    if n_spread:
+        total = p.batch * p.heads_kv * nb
+        step = max(1, total // n_spread) | 1  # odd: the blocks of every slab fall at varied positions
+        for u in range(step // 2, total, step):
+            units.add((u // (p.heads_kv * nb), (u // nb) % p.heads_kv, u % nb))
     return sorted(units)
+
+
+# units checked against the oracle per workload beyond the planted, edge and
+# random ones (the oracle's cost per unit grows with the rows and keys it attends)
+SPREAD = {2: 512, 3: 256, 5: 64}
 
 
 @pytest.mark.timeout(900)
@@ -76,11 +91,12 @@ def test_full_prefill(workload_id):
     log(f"  {oc.size} selections bit-exact; smallest relative boundary margin "
         f"{min(rel) if rel else float('nan'):.2e}; planted blocks dropped by coarse levels: {dropped}; "
         "oracle attention on sampled blocks")
-    units = _sample_units(p, man) if workload_id != 1 else None
+    units = _sample_units(p, man, n_spread=SPREAD[workload_id]) if workload_id != 1 else None
     o, ol = oracle.attend(qh, kh, vh, oi, oc, p.sink_len, p.block_size, p.scale, blocks=units)
     err = assert_outputs_close(p, to_host(out), o, to_host(lse), ol)
     found = sum(1 for n in man["needles"] if n["survived"] and n["target"] in oi[n["b"], n["g"], n["qb"]].tolist())
-    log(f"  max abs err {err:.2e}; planted blocks selected: {found}/{sum(n['survived'] for n in man['needles'])}")
+    log(f"  {len(units) if units else 'all'} units: max abs err {err:.2e}; planted blocks selected: "
+        f"{found}/{sum(n['survived'] for n in man['needles'])}")
 
 
 @pytest.mark.timeout(900)
