@@ -14,11 +14,14 @@
 // (batch, kv head, query block) unit -- rows of all heads in the GQA group --
 // so every K/V tile staged in LDS feeds up to 256 rows. Tiles arrive by
 // asynchronous global->LDS copies into two stages, the next tile in flight while
-// the current one is computed (units of at most 64 rows: one stage, four
-// workgroups per compute unit covering each other's copies). Per tile each wave computes S^T = K Q^T with
-// v_mfma_f32_32x32x16_bf16 (a lane then owns one query column), runs the
-// online softmax in registers, and accumulates O^T += V^T P^T on the same
-// matrix cores, reading V^T fragments with gfx950's transposing LDS reads.
+// the current one is computed. Units of at most 64 rows take one stage of
+// unpadded (swizzled, at d = 128) tiles, split by phase: the next tile's keys
+// load during this tile's softmax and value product, its values during its own
+// scores; four such workgroups share a compute unit. Per tile each wave computes
+// S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (a lane then owns one query
+// column), runs the online softmax in registers, and accumulates O^T += V^T P^T
+// on the same matrix cores, reading V^T fragments with gfx950's transposing LDS
+// reads.
 // fp32 path: plain VALU, one thread per query row.
 #include <algorithm>
 

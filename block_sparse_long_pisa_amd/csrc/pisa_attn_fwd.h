@@ -227,13 +227,12 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
   int j, nvalid;
   bool local;
   walk.at(0, sel, g, qb, local_rows, j, nvalid, local);
-  issue_tile(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
-                        wave, plan);
+  issue_tile(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0, wave, plan);
   if constexpr (ST == 1) {
     // One stage, split by phase: the keys of tile t + 1 load while tile t's
     // softmax and value product run, its values while tile t + 1's scores run.
     // Each wave's copies complete in the order issued (K before V), so waiting
-    // until at most VMIN of its copies are outstanding -- fewer than the V
+    // until at most VMIN of its copies are outstanding -- no more than the V
     // copies it issued after them -- means its K copies have landed.
     static_assert(BS <= 64, "a one-stage tile is one chunk of keys");
     constexpr int VMIN = TilePitch<D, BS, SW>::VI / NW;
@@ -267,8 +266,8 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
     bool loc1 = false;
     if (t + 1 < walk.ntiles) {
       walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
-      issue_tile(kbase + (int64_t)j1 * BS * D, vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K1,
-                            V1, wave, plan);
+      issue_tile(kbase + (int64_t)j1 * BS * D, vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K1, V1,
+                 wave, plan);
     }
     compute_tile(st, K0, V0, nvalid, local, j * BS, qpos, hi, c, wg_qmax);
     if (t + 1 >= walk.ntiles) break;
@@ -277,7 +276,7 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
     if (t + 2 < walk.ntiles) {
       walk.at(t + 2, sel, g, qb, local_rows, j, nvalid, local);
       issue_tile(kbase + (int64_t)j * BS * D, vbase + (int64_t)j * BS * D, min(BS, g.N - j * BS), K0, V0,
-                            wave, plan);
+                 wave, plan);
     }
     compute_tile(st, K1, V1, nv1, loc1, j1 * BS, qpos, hi, c, wg_qmax);
   }
