@@ -69,18 +69,36 @@ __device__ __forceinline__ void tile_scores(const AttnState<D, BS, SW>& st, cons
   constexpr int NDS = D / 16;
   constexpr int KC = kChunk<BS>;
   constexpr int NKB = KC / 32;
+  // the chunk's K fragments in product order (32-key block kb, step ds); PD
+  // reads are kept in flight ahead of the product that takes them
+  constexpr int NF = NKB * NDS;
+  constexpr int PD = NF < 4 ? NF : 4;
   const char* kb_base = reinterpret_cast<const char*>(ks);
+  auto frag = [&](int f) {
+    return *reinterpret_cast<const bf16x8_t*>(kb_base + st.k_at(f % NDS) +
+                                              (ch * KC + (f / NDS) * 32) * TilePitch<D, BS, SW>::K * 2);
+  };
+  bf16x8_t a[PD];
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
+  for (int f = 0; f < PD; ++f) a[f] = frag(f);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+  for (int f = 0; f < NF; ++f) {
+    const int kb = f / NDS;
+    if (f % NDS == 0)
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb_base + st.k_at(ds) +
-                                                            (ch * KC + kb * 32) * TilePitch<D, BS, SW>::K * 2);
-      sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, st.qf[ds], sacc[kb], 0, 0, 0);
-    }
+      for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[f % PD], st.qf[f % NDS], sacc[kb], 0, 0, 0);
+    if (f + PD < NF) a[f % PD] = frag(f + PD);
   }
+  // hold the schedule to that order (the compiler would otherwise keep fewer
+  // reads in flight): PD reads, then one product per further read
+  __builtin_amdgcn_sched_group_barrier(0x100, PD, 0);
+#pragma unroll
+  for (int f = PD; f < NF; ++f) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PD, 0);
   if (__builtin_expect(local || nvalid < BS, 0)) {  // uniform across the workgroup
     // keys of this tile beyond `lim` are masked (partial block, causal diagonal)
     const int lim = min(nvalid - 1, local ? qpos - key0 : BS - 1) - (ch * KC + hi * 4);
@@ -122,6 +140,22 @@ __device__ __forceinline__ void tile_update(AttnState<D, BS, SW>& st, f32x16_t (
       for (int i = 0; i < 16; ++i) st.oacc[db][i] *= alpha;
   }
   st.m_run = m_ref;
+  // the chunk's V^T fragments in product order (32-key block kb, 16-key half
+  // hh, 32-column slice db); PV reads are kept in flight ahead of the product
+  // that takes them, and the first PV load while the exponentials are computed
+  constexpr int NV = NKB * 2 * NDB;
+  constexpr int PV = NV < 4 ? NV : 4;
+  auto vfrag = [&](int f) {
+    const int kb = f / (2 * NDB), hh = (f / NDB) % 2, db = f % NDB;
+    const int step = (ch * KC + kb * 32 + hh * 16) * TilePitch<D, BS, SW>::V * 2;
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vb_base + st.v_lo(db) + step));
+    const v4i16_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vb_base + st.v_up(db) + step));
+    const v4i16_t a8[2] = {lo, up};
+    return __builtin_bit_cast(bf16x8_t, a8);
+  };
+  bf16x8_t va[PV];
+#pragma unroll
+  for (int f = 0; f < PV; ++f) va[f] = vfrag(f);
   float rs = 0.f;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
@@ -140,14 +174,11 @@ __device__ __forceinline__ void tile_update(AttnState<D, BS, SW>& st, f32x16_t (
       bf16x8_t pb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = (__bf16)sacc[kb][hh * 8 + e];
-      const int step = (ch * KC + kb * 32 + hh * 16) * TilePitch<D, BS, SW>::V * 2;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vb_base + st.v_lo(db) + step));
-        const v4i16_t up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(vb_base + st.v_up(db) + step));
-        const v4i16_t a8[2] = {lo, up};
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a8);
-        st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, st.oacc[db], 0, 0, 0);
+        const int f = (kb * 2 + hh) * NDB + db;
+        st.oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[f % PV], pb, st.oacc[db], 0, 0, 0);
+        if (f + PV < NV) va[f % PV] = vfrag(f + PV);
       }
     }
   }
