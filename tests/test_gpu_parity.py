@@ -70,6 +70,26 @@ def test_prefill_parity(name):
     log(f"  max abs err {err:.2e}")
 
 
+# every (head dim, block, waves per unit) the bf16 attention is built for: the
+# library takes 8 waves when the unit's (head, 32-row) pairs G*bs/32 are a
+# multiple of 8, else 4, 2 or 1, so G = NW*32/bs picks each one
+SHAPES = [(d, bs, nw) for d in (64, 128) for bs in (32, 64, 128) for nw in (8, 4, 2, 1) if nw * 32 >= bs]
+
+
+@pytest.mark.parametrize("d,bs,nw", SHAPES)
+def test_every_attention_shape(d, bs, nw):
+    G = nw * 32 // bs
+    p = P(1, 2 * G, 2, 11 * bs + 37, d, bs, 4, 2, 3, 64, "bf16")
+    log(f"attention shape d={d} bs={bs} waves={nw}: {p}")
+    q, k, v, _ = _inputs(p, ("uniform_pairs", 2), None, seed=23)
+    levels, gi, gc, out, lse = gpu_prefill(p, to_dev(q, p.dtype), to_dev(k, p.dtype), to_dev(v, p.dtype))
+    pyr, oi, oc = oracle_select(p, q, k)
+    assert_selection_equal(gi, gc, oi, oc)
+    o, ol = oracle.attend(q, k, v, oi, oc, p.sink_len, p.block_size, p.scale)
+    err = assert_outputs_close(p, to_host(out), o, lse, ol)
+    log(f"  max abs err {err:.2e}")
+
+
 def test_all_blocks_selected_is_dense_attention():
     p = P(1, 4, 2, 1024, 128, 64, 4, 2, 16, 0, "bf16")
     q, k, v, _ = _inputs(p, None, SHARP)
