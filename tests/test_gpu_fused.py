@@ -18,7 +18,7 @@ import gen
 import oracle
 from parity import assert_outputs_close, assert_selection_equal, cprob, log, oracle_select, to_dev, to_host
 from test_gpu_full import _sample_units
-from test_gpu_parity import SMALL
+from test_gpu_parity import SHAPES, SMALL
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -48,6 +48,22 @@ def test_fused_parity(name):
     q, k, v, _ = gen.host_inputs(p, 11, s, plant)
     cp = cprob(p)
     out, lse, idx, cnt = _both(pisa, cp, to_dev(q, p.dtype), to_dev(k, p.dtype), to_dev(v, p.dtype))
+    _, oi, oc = oracle_select(p, q, k)
+    assert_selection_equal(to_host(idx), to_host(cnt), oi, oc)
+    o, ol = oracle.attend(q, k, v, oi, oc, p.sink_len, p.block_size, p.scale)
+    err = assert_outputs_close(p, to_host(out), o, to_host(lse), ol)
+    log(f"  max abs err {err:.2e}")
+
+
+@pytest.mark.parametrize("d,bs,nw", SHAPES)
+def test_fused_every_attention_shape(d, bs, nw):
+    import block_sparse_long_pisa_amd as pisa
+
+    G = nw * 32 // bs
+    p = gen.Problem(1, 2 * G, 2, 11 * bs + 37, d, bs, 4, 2, 3, 64, "bf16")
+    log(f"fused shape d={d} bs={bs} waves={nw}: {p}")
+    q, k, v, _ = gen.host_inputs(p, 23, 1.0 / math.sqrt(d), ("uniform_pairs", 2))
+    out, lse, idx, cnt = _both(pisa, cprob(p), to_dev(q, p.dtype), to_dev(k, p.dtype), to_dev(v, p.dtype))
     _, oi, oc = oracle_select(p, q, k)
     assert_selection_equal(to_host(idx), to_host(cnt), oi, oc)
     o, ol = oracle.attend(q, k, v, oi, oc, p.sink_len, p.block_size, p.scale)
