@@ -267,24 +267,29 @@ __device__ __forceinline__ void attend_unit(const Geo& g, const uint16_t* __rest
     // copies it issued after them -- means its K copies have landed.
     static_assert(BS <= 64, "a one-stage tile is one chunk of keys");
     constexpr int VMIN = TilePitch<D, BS, SW>::VI / NW;
+    // the query fragments, loaded before the first tile's copies, have landed
+    wait_loads<TilePitch<D, BS, SW>::KI / NW + VMIN>();
     for (int t = 0; t < walk.ntiles; ++t) {
       wait_loads<VMIN>();
-      __syncthreads();  // K(t) has landed for every wave
+      lds_read_barrier();  // K(t) has landed for every wave (no fence: V(t) keeps loading)
       f32x16_t sacc[BS / 32];
       tile_scores(st, K0, 0, nvalid, local, j * BS, qpos, hi, sacc);
       wait_loads<0>();
-      __syncthreads();  // V(t) has landed; every wave is done with K(t)
+      lds_read_barrier();  // V(t) has landed; every wave is done with K(t)
+      // The copies are issued on every tile, past the last one with an empty
+      // range (the hardware then writes zeros and reads nothing): with copies
+      // into LDS issued on some paths only, the compiler waits for all of them
+      // before any LDS read of the next tile, which would leave V(t + 1) no
+      // scores to hide behind.
       const bool more = t + 1 < walk.ntiles;
       int j1 = j, nv1 = 0;
       bool loc1 = false;
-      if (more) {
-        walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
-        issue_half<true>(kbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), K0, wave, plan);
-      }
+      if (more) walk.at(t + 1, sel, g, qb, local_rows, j1, nv1, loc1);
+      const int rows1 = more ? min(BS, g.N - j1 * BS) : 0;
+      issue_half<true>(kbase + (int64_t)j1 * BS * D, rows1, K0, wave, plan);
       tile_update(st, sacc, V0, 0, c);
-      if (!more) break;
       lds_read_barrier();  // every wave is done with V(t); K(t + 1) keeps loading
-      issue_half<false>(vbase + (int64_t)j1 * BS * D, min(BS, g.N - j1 * BS), V0, wave, plan);
+      issue_half<false>(vbase + (int64_t)j1 * BS * D, rows1, V0, wave, plan);
       j = j1;
       nvalid = nv1;
       local = loc1;
