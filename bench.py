@@ -29,20 +29,20 @@ BF16_PEAK = 2.5e15  # flop/s, dense bf16 matrix cores
 # HBM traffic per launch on these two workloads, from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch). Each counter is scaled by what
 # it reads for a plain device copy of 1 GiB into 1 GiB: FETCH_SIZE reports
-# 524335.9 KiB for the copy's 1 GiB of reads, WRITE_SIZE 1048576 KiB for its
+# 524339.1 KiB for the copy's 1 GiB of reads, WRITE_SIZE 1048576 KiB for its
 # writes. A figure holds only for the kernel source it was taken on: the sources
 # are hashed at run time and a changed kernel reports null.
-COPY_SCALE = {"fetch": 1048576.0 / 524335.9375, "write": 1048576.0 / 1048576.0}
+COPY_SCALE = {"fetch": 1048576.0 / 524339.125, "write": 1048576.0 / 1048576.0}
 MEASURED_TRAFFIC = {
     # step: (sources, sha256 prefix of their bytes in this order, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "42bc992c54b96a69",
-                  5816996.5, 1048579.1),
+    "attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "1b401d98a4eb06a6",
+                  5823591.2, 1048576.5),
     "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "88eed11ade081425",
                 131123.5 + 275.7, 4608.1 + 72.0),  # leaf and level 1, then levels 2 and up
     "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "5d34d5121909d47d",
                526688.2, 1056.1),
     "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h"), "9312885314af25df",
-               47862.6 + 546244.4 + 3601.1, 80.0 + 6336.0 + 512.0),  # select + split attention + merge
+               47865.1 + 546245.5 + 3601.1, 80.0 + 6336.0 + 512.0),  # select + split attention + merge
 }
 
 
