@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <string>
@@ -130,6 +131,25 @@ hipError_t device_cus(int* cus) {
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   return hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+}
+
+bool log_launches() {
+  static const bool on = [] {
+    const char* e = getenv("PISA_LOG");
+    return e != nullptr && *e != 0 && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void log_launch(const Geo& g, const char* kernel, const char* launcher, dim3 grid, dim3 block) {
+  // the launcher's template arguments, as its signature prints them: "[D = 128, ...]"
+  const char* targs = strrchr(launcher, '[');
+  fprintf(stderr,
+          "[pisa] launch %s %s grid (%u, %u, %u) workgroup (%u, %u, %u) | B %d Hq %d Hkv %d N %d d %d bs %d f %d L %d "
+          "K %d sink %d %s %s %s\n",
+          kernel, targs ? targs : "", grid.x, grid.y, grid.z, block.x, block.y, block.z, g.B, g.Hq, g.Hkv, g.N, g.D,
+          g.bs, g.f, g.L, g.K, g.sink, g.dtype == PISA_BF16 ? "bf16" : "f32", g.causal ? "causal" : "bidirectional",
+          g.pool == PISA_POOL_MAX ? "max-pool" : "mean-pool");
 }
 
 }  // namespace pisa

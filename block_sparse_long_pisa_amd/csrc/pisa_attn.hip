@@ -179,7 +179,7 @@ hipError_t launch_bf16(const Geo& g, const void* q, const void* k, const void* v
   // over the whole GPU (1); few -- slab-fastest (0)
   const int slabs = g.B * g.Hkv;
   const int order = slabs % 8 == 0 && grid % 8 == 0 ? 2 : slabs > 8 ? 1 : 0;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, BS, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, g,
+  PISA_LAUNCH(g, (attn_bf16_kernel<D, BS, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, g,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, (uint16_t*)out, lse, parts,
                      order);
   return hipGetLastError();
@@ -219,10 +219,10 @@ hipError_t launch_attn(const Geo& g, const void* q, const void* k, const void* v
                       : launch_bf16_bs<64>(g, q, k, v, idx, cnt, out, lse, s);
   dim3 grid(g.nb, g.Hq, g.B);
   if (g.D == 128)
-    hipLaunchKernelGGL((attn_f32_kernel<128>), grid, dim3(g.bs), 0, s, g, (const float*)q, (const float*)k,
+    PISA_LAUNCH(g, (attn_f32_kernel<128>), grid, dim3(g.bs), 0, s, g, (const float*)q, (const float*)k,
                        (const float*)v, idx, cnt, (float*)out, lse);
   else
-    hipLaunchKernelGGL((attn_f32_kernel<64>), grid, dim3(g.bs), 0, s, g, (const float*)q, (const float*)k,
+    PISA_LAUNCH(g, (attn_f32_kernel<64>), grid, dim3(g.bs), 0, s, g, (const float*)q, (const float*)k,
                        (const float*)v, idx, cnt, (float*)out, lse);
   return hipGetLastError();
 }

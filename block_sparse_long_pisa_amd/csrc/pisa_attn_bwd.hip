@@ -821,25 +821,25 @@ hipError_t launch_bwd_t(const Geo& g, const void* q, const void* k, const void* 
   const int parts = waves / nw;
   const unsigned grid = (unsigned)((int64_t)g.nb * g.B * g.Hkv * parts);
   switch (nw) {
-    case 8: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 8>), dim3(grid), dim3(512), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
-    case 4: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 4>), dim3(grid), dim3(256), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
-    case 2: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 2>), dim3(grid), dim3(128), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
-    default: hipLaunchKernelGGL((bwd_dq_kernel<D, BS, 1>), dim3(grid), dim3(64), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
+    case 8: PISA_LAUNCH(g, (bwd_dq_kernel<D, BS, 8>), dim3(grid), dim3(512), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
+    case 4: PISA_LAUNCH(g, (bwd_dq_kernel<D, BS, 4>), dim3(grid), dim3(256), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
+    case 2: PISA_LAUNCH(g, (bwd_dq_kernel<D, BS, 2>), dim3(grid), dim3(128), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
+    default: PISA_LAUNCH(g, (bwd_dq_kernel<D, BS, 1>), dim3(grid), dim3(64), 0, s, g, qt, kt, vt, idx, cnt, dot, ot, lse, w.rowdot, w.lse2, (uint16_t*)dq, parts); break;
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_list_kernel, dim3((unsigned)z.nkb), dim3(kListThreads), 0, s, g, idx, cnt, w.counts,
+  PISA_LAUNCH(g, bwd_list_kernel, dim3((unsigned)z.nkb), dim3(kListThreads), 0, s, g, idx, cnt, w.counts,
                      (const int32_t*)nullptr, (int32_t*)nullptr, 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, s, w.counts, (int)z.nkb, w.list_off, w.seg_off);
+  PISA_LAUNCH(g, bwd_scan_kernel, dim3(1), dim3(1024), 0, s, w.counts, (int)z.nkb, w.list_off, w.seg_off);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_list_kernel, dim3((unsigned)z.nkb), dim3(kListThreads), 0, s, g, idx, cnt, w.counts,
+  PISA_LAUNCH(g, bwd_list_kernel, dim3((unsigned)z.nkb), dim3(kListThreads), 0, s, g, idx, cnt, w.counts,
                      w.list_off, w.lists, 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_kv_kernel<D, BS>), dim3((unsigned)z.max_segs), dim3(BS / 16 * 64), 0, s, g, qt, kt, vt, dot,
+  PISA_LAUNCH(g, (bwd_kv_kernel<D, BS>), dim3((unsigned)z.max_segs), dim3(BS / 16 * 64), 0, s, g, qt, kt, vt, dot,
                      w.lse2, w.rowdot, w.lists, w.list_off, w.seg_off, (int)z.nkb, w.pdk, w.pdv, (uint16_t*)dk,
                      (uint16_t*)dv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_kv_reduce_kernel<D>), dim3((unsigned)z.nkb), dim3(256), 0, s, g, w.seg_off, w.pdk, w.pdv,
+  PISA_LAUNCH(g, (bwd_kv_reduce_kernel<D>), dim3((unsigned)z.nkb), dim3(256), 0, s, g, w.seg_off, w.pdk, w.pdv,
                      (uint16_t*)dk, (uint16_t*)dv);
   return hipGetLastError();
 }

@@ -441,22 +441,22 @@ static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, c
     const int e = pool_slots_per_lane(g);
     const T* qt = (const T*)q;
     if (e <= 2)
-      hipLaunchKernelGGL((decode_select_kernel<T, D, 2>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+      PISA_LAUNCH(g, (decode_select_kernel<T, D, 2>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
                          len_all, ws.idx, ws.cnt);
     else if (e <= 4)
-      hipLaunchKernelGGL((decode_select_kernel<T, D, 4>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+      PISA_LAUNCH(g, (decode_select_kernel<T, D, 4>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
                          len_all, ws.idx, ws.cnt);
     else if (e <= 5)  // K = 32 at fanout 8: 263 slots (the ranking's bit counts run over fewer slot groups)
-      hipLaunchKernelGGL((decode_select_kernel<T, D, 5>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+      PISA_LAUNCH(g, (decode_select_kernel<T, D, 5>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
                          len_all, ws.idx, ws.cnt);
     else if (e <= 6)
-      hipLaunchKernelGGL((decode_select_kernel<T, D, 6>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+      PISA_LAUNCH(g, (decode_select_kernel<T, D, 6>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
                          len_all, ws.idx, ws.cnt);
     else if (e <= 8)
-      hipLaunchKernelGGL((decode_select_kernel<T, D, 8>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+      PISA_LAUNCH(g, (decode_select_kernel<T, D, 8>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
                          len_all, ws.idx, ws.cnt);
     else
-      hipLaunchKernelGGL((decode_select_kernel<T, D, 16>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
+      PISA_LAUNCH(g, (decode_select_kernel<T, D, 16>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
                          len_all, ws.idx, ws.cnt);
   }
   hipError_t e = hipGetLastError();
@@ -466,14 +466,14 @@ static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, c
   const T* kt = (const T*)kc;
   const T* vt = (const T*)vc;
   switch (g.G) {
-    case 1: hipLaunchKernelGGL((decode_attn_kernel<T, D, 1>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
-    case 2: hipLaunchKernelGGL((decode_attn_kernel<T, D, 2>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
-    case 4: hipLaunchKernelGGL((decode_attn_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
-    default: hipLaunchKernelGGL((decode_attn_kernel<T, D, 8>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
+    case 1: PISA_LAUNCH(g, (decode_attn_kernel<T, D, 1>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
+    case 2: PISA_LAUNCH(g, (decode_attn_kernel<T, D, 2>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
+    case 4: PISA_LAUNCH(g, (decode_attn_kernel<T, D, 4>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
+    default: PISA_LAUNCH(g, (decode_attn_kernel<T, D, 8>), grid, dim3(kDecThreads), 0, s, g, qt, kt, vt, lens, len_all, splits, ws); break;
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(g.B * g.Hq), dim3(D), 0, s, g, splits, ws, (T*)out, lse);
+  PISA_LAUNCH(g, (decode_merge_kernel<T, D>), dim3(g.B * g.Hq), dim3(D), 0, s, g, splits, ws, (T*)out, lse);
   return hipGetLastError();
 }
 

@@ -125,7 +125,7 @@ hipError_t launch_fused(const Geo& g, const void* q, const void* k, const void* 
                         int32_t* cnt, void* out, float* lse, hipStream_t s) {
   const int parts = g.G * BS / 32 / NW;
   const int64_t grid = (int64_t)g.nb * g.B * g.Hkv * parts;
-  hipLaunchKernelGGL((select_attn_bf16_kernel<D, BS, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, g,
+  PISA_LAUNCH(g, (select_attn_bf16_kernel<D, BS, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, g,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, pyr, idx, cnt, (uint16_t*)out, lse,
                      parts);
   return hipGetLastError();

@@ -88,6 +88,17 @@ struct Wide<float> {
 // compute units of the current device (the runtime's cached attribute)
 hipError_t device_cus(int* cus);
 
+// Launch log: with PISA_LOG set to anything but 0 in the environment, every
+// kernel launch is described on stderr (kernel, template arguments of its
+// launcher, grid, workgroup, problem) just before it is enqueued.
+bool log_launches();
+void log_launch(const Geo& g, const char* kernel, const char* launcher, dim3 grid, dim3 block);
+#define PISA_LAUNCH(g, kernel, grid, block, shmem, stream, ...)                                          \
+  do {                                                                                                  \
+    if (::pisa::log_launches()) ::pisa::log_launch(g, #kernel, __PRETTY_FUNCTION__, dim3(grid), dim3(block)); \
+    hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                                \
+  } while (0)
+
 // ---------------------------------------------------------------------------
 // launchers (each lives beside its kernels)
 

@@ -290,9 +290,9 @@ template <int D, bool MX, int F>
 hipError_t launch_upper_f(const Geo& g, float* pyr, int lo, int top, hipStream_t s) {
   const dim3 grid(g.nodes[top], g.B * g.Hkv);
   if (g.span[top] / g.span[lo] <= kUpperThreads / D)
-    hipLaunchKernelGGL((pool_upper_kernel<D, MX, F, 1>), grid, dim3(kUpperThreads), 0, s, g, pyr, lo, top);
+    PISA_LAUNCH(g, (pool_upper_kernel<D, MX, F, 1>), grid, dim3(kUpperThreads), 0, s, g, pyr, lo, top);
   else
-    hipLaunchKernelGGL((pool_upper_kernel<D, MX, F, kUpperNodes<F>>), grid, dim3(kUpperThreads), 0, s, g, pyr, lo,
+    PISA_LAUNCH(g, (pool_upper_kernel<D, MX, F, kUpperNodes<F>>), grid, dim3(kUpperThreads), 0, s, g, pyr, lo,
                        top);
   return hipGetLastError();
 }
@@ -322,7 +322,7 @@ hipError_t launch_upper(const Geo& g, float* pyr, hipStream_t s) {
 template <typename T, int D, bool MX>
 hipError_t launch_append_m(const Geo& g, const void* k, float* pyr, const int32_t* old_lens, const int32_t* new_lens,
                            hipStream_t s) {
-  hipLaunchKernelGGL((pool_append_kernel<T, D, MX>), dim3(g.B * g.Hkv), dim3(kPoolThreads), 0, s, g, (const T*)k, pyr,
+  PISA_LAUNCH(g, (pool_append_kernel<T, D, MX>), dim3(g.B * g.Hkv), dim3(kPoolThreads), 0, s, g, (const T*)k, pyr,
                      old_lens, new_lens);
   return hipGetLastError();
 }
@@ -339,7 +339,7 @@ hipError_t launch_pool_m(const Geo& g, const void* k, float* pyr, hipStream_t s)
   const int slabs = g.B * g.Hkv;
   const int chunk = g.L >= 2 ? g.f : 8;
   dim3 grid((g.nb + chunk - 1) / chunk, slabs);
-  hipLaunchKernelGGL((pool_leaf_kernel<T, D, MX>), grid, dim3(kPoolThreads), 0, s, g, (const T*)k, pyr, chunk);
+  PISA_LAUNCH(g, (pool_leaf_kernel<T, D, MX>), grid, dim3(kPoolThreads), 0, s, g, (const T*)k, pyr, chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g.L < 3) return hipSuccess;

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kSelectThreads) __attribute__((amdgpu_waves_per_eu(
 template <typename T, int D, int E>
 hipError_t launch_select_e(const Geo& g, const void* q, const float* pyr, int32_t* idx, int32_t* cnt, hipStream_t s) {
   const int blocks = g.B * g.Hkv * ((g.nb + kSelectWaves - 1) / kSelectWaves);
-  hipLaunchKernelGGL((select_kernel<T, D, E>), dim3(blocks), dim3(kSelectThreads), 0, s, g, (const T*)q, pyr, idx, cnt);
+  PISA_LAUNCH(g, (select_kernel<T, D, E>), dim3(blocks), dim3(kSelectThreads), 0, s, g, (const T*)q, pyr, idx, cnt);
   return hipGetLastError();
 }
 

@@ -35,6 +35,10 @@
  *     pisa_last_error() then holds a description (per calling thread). A fault
  *     inside a kernel surfaces at the caller's next synchronisation.
  *   - An empty problem (batch == 0 or seq_len == 0) is valid and launches nothing.
+ *   - Diagnostics: with the environment variable PISA_LOG set to anything but 0
+ *     when the library is first used, every kernel launch is described on
+ *     stderr (kernel, its template arguments, grid, workgroup and problem) just
+ *     before it is enqueued; nothing else changes.
  */
 #ifndef PISA_H
 #define PISA_H
