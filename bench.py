@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK = 8.0e12  # B/s, MI355X
 BF16_PEAK = 2.5e15  # flop/s, dense bf16 matrix cores
 
-# HBM traffic per launch on these two workloads, from two rocprofv3 --pmc runs
+# HBM traffic per launch on the 128K prefill and the 64 x 128K decode (and, keyed
+# "w2/..." and "w5/...", on the 32K and 1M prefills), from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch). Each counter is scaled by what
 # it reads for a plain device copy of 1 GiB into 1 GiB: FETCH_SIZE reports
 # 524339.1 KiB for the copy's 1 GiB of reads, WRITE_SIZE 1048576 KiB for its
@@ -35,21 +36,35 @@ BF16_PEAK = 2.5e15  # flop/s, dense bf16 matrix cores
 COPY_SCALE = {"fetch": 1048576.0 / 524339.125, "write": 1048576.0 / 1048576.0}
 MEASURED_TRAFFIC = {
     # step: (sources, sha256 prefix of their bytes in this order, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "1b401d98a4eb06a6",
+    "attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "80f94ff34b953353",
                   5823591.2, 1048576.5),
-    "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "88eed11ade081425",
+    "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "02af82e0273fed3e",
                 131123.5 + 275.7, 4608.1 + 72.0),  # leaf and level 1, then levels 2 and up
-    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "5d34d5121909d47d",
+    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "f5714ab61c27b527",
                526688.2, 1056.1),
-    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h"), "9312885314af25df",
+    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h"), "edb753a70fb348ad",
                47865.1 + 546245.5 + 3601.1, 80.0 + 6336.0 + 512.0),  # select + split attention + merge
+    # the 32K MHA (w2) and 1M one-group (w5) prefills, from the same runs
+    "w2/attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "80f94ff34b953353",
+                     2598850.3, 263646.5),
+    "w2/pyramid": (("pisa_pool.hip", "pisa_internal.h"), "02af82e0273fed3e", 131123.4 + 531.7, 9216.0 + 128.0),
+    "w2/select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "f5714ab61c27b527",
+                  135745.4, 1088.6),
+    "w5/attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "80f94ff34b953353",
+                     29777662.3, 1048622.3),
+    "w5/pyramid": (("pisa_pool.hip", "pisa_internal.h"), "02af82e0273fed3e", 131123.9 + 8.9 + 275.7, 4608.4 + 1.0 + 72.0),
+    "w5/select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "f5714ab61c27b527",
+                  543212.3, 2125.1),
 }
 
 
 def measured_traffic(step):
-    """Scaled HBM bytes (read + written) of one launch of `step`, or None if its kernel changed since."""
+    """Scaled HBM bytes (read + written) of one launch of `step` ("attention", or "w2/attention" for another
+    workload), or None if it was not measured or its kernel changed since."""
     import hashlib
 
+    if step not in MEASURED_TRAFFIC:
+        return None
     files, digest, fetch_kib, write_kib = MEASURED_TRAFFIC[step]
     h = hashlib.sha256()
     for f in files:
@@ -352,13 +367,13 @@ def time_prefill(p, cp, q, k, v, pyr, idx, cnt, out, steps, warmup):
     return elapsed / steps, t_pool, t_sel, t_att
 
 
-def kernel_lines(p, nodes, idx, cnt, t_pool, t_sel, t_att, traffic=True):
+def kernel_lines(p, nodes, idx, cnt, t_pool, t_sel, t_att, workload=None):
     idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
     pairs = attended_pairs(p, idx_h, cnt_h)
     flops = 4.0 * p.head_dim * pairs
     b_pool = pyramid_bytes(p, nodes)
     b_sel = select_bytes(p, nodes)
-    tr = measured_traffic if traffic else (lambda _: None)
+    tr = (lambda step: measured_traffic(f"{workload}/{step}")) if workload else measured_traffic
     return flops, pairs, {
         "pyramid": {"ms": t_pool * 1e3, "bound": "hbm", "bytes": b_pool, "GB/s": b_pool / t_pool / 1e9,
                     "frac": b_pool / t_pool / HBM_PEAK, "traffic": tr("pyramid")},
@@ -397,7 +412,7 @@ def run_other_prefill(wid, args, dev):
     out = torch.empty_like(q)
     steps = args.workload_steps
     t_step, t_pool, t_sel, t_att = time_prefill(p, cp, q, k, v, pyr, idx, cnt, out, steps, args.warmup)
-    flops, pairs, kernels = kernel_lines(p, nodes, idx, cnt, t_pool, t_sel, t_att, traffic=False)
+    flops, pairs, kernels = kernel_lines(p, nodes, idx, cnt, t_pool, t_sel, t_att, workload=f"w{wid}")
     log(f"workload {wid}: {t_step * 1e3:.3f} ms/step: pyramid {t_pool * 1e3:.3f} ms "
         f"({kernels['pyramid']['frac'] * 100:.0f}% HBM), select {t_sel * 1e3:.3f} ms "
         f"({kernels['select']['frac'] * 100:.0f}% HBM), attention {t_att * 1e3:.3f} ms "

@@ -1,4 +1,5 @@
-"""The bench's algorithmic-work counts agree with the oracle's attended sets and descent pools."""
+"""The bench's algorithmic-work counts agree with the oracle's attended sets and descent pools; its
+measured-traffic table holds only for the sources it was taken on."""
 
 import numpy as np
 
@@ -68,3 +69,22 @@ def test_median_ms_takes_the_median_of_event_intervals():
 
     pairs = [(Ev(0.0), Ev(d)) for d in (5.0, 1.0, 100.0, 2.0, 3.0)]
     assert bench.median_ms(pairs) == 3.0e-3
+
+
+def test_measured_traffic_holds_only_for_the_sources_it_was_taken_on(monkeypatch):
+    import hashlib
+    import os
+
+    import bench
+
+    files = ("pisa_pool.hip", "pisa_internal.h")
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(bench.ROOT, "block_sparse_long_pisa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    table = {"x": (files, h.hexdigest()[:16], 100.0, 10.0), "y": (files, "0" * 16, 100.0, 10.0)}
+    monkeypatch.setattr(bench, "MEASURED_TRAFFIC", table)
+    monkeypatch.setattr(bench, "COPY_SCALE", {"fetch": 2.0, "write": 1.0})
+    assert bench.measured_traffic("x") == 1024 * (100 * 2 + 10)
+    assert bench.measured_traffic("y") is None  # another source
+    assert bench.measured_traffic("w2/x") is None  # never measured
