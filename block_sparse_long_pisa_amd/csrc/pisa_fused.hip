@@ -134,11 +134,16 @@ hipError_t launch_fused(const Geo& g, const void* q, const void* k, const void* 
 template <int D, int BS>
 hipError_t launch_fused_nw(const Geo& g, const void* q, const void* k, const void* v, const float* pyr, int32_t* idx,
                            int32_t* cnt, void* out, float* lse, hipStream_t s) {
-  const int pairs = g.G * BS / 32;  // (head, 32-query chunk) pairs per unit
+  // (head, 32-query chunk) pairs per unit: a multiple of BS / 32, so blocks of
+  // 128 take 4 or 8 waves and blocks of 64 at least 2 (the others are not built)
+  const int pairs = g.G * BS / 32;
   if (pairs % 8 == 0) return launch_fused<D, BS, 8>(g, q, k, v, pyr, idx, cnt, out, lse, s);
   if (pairs % 4 == 0) return launch_fused<D, BS, 4>(g, q, k, v, pyr, idx, cnt, out, lse, s);
-  if (pairs % 2 == 0) return launch_fused<D, BS, 2>(g, q, k, v, pyr, idx, cnt, out, lse, s);
-  return launch_fused<D, BS, 1>(g, q, k, v, pyr, idx, cnt, out, lse, s);
+  if constexpr (BS <= 64) {
+    if (pairs % 2 == 0) return launch_fused<D, BS, 2>(g, q, k, v, pyr, idx, cnt, out, lse, s);
+    if constexpr (BS <= 32) return launch_fused<D, BS, 1>(g, q, k, v, pyr, idx, cnt, out, lse, s);
+  }
+  return hipErrorInvalidValue;  // not reached: see above
 }
 
 template <int D>
