@@ -96,3 +96,21 @@ def assert_outputs_close(p: gen.Problem, o_gpu: np.ndarray, o_ora: np.ndarray, l
         d = np.abs(lse_gpu[m].astype(np.float64) - lse_ora[m]).max() if a.size else 0.0
         assert d <= LSE_ABS[p.dtype], f"lse error {d:.3e}"
     return err
+
+
+GRAD_REL_L2 = 1e-2  # backward (bf16): per-tensor relative L2 error
+GRAD_MAX_REL = 1e-2  # backward (bf16): max-abs error as a fraction of the tensor's largest gradient
+
+
+def grads_close(name: str, got: np.ndarray, want: np.ndarray):
+    """Backward bar: p and dS enter the products rounded to bf16 (relative 2^-9
+    each), D_i uses the forward's bf16 output and the gradients are rounded to
+    bf16 on output; summed over many keys the roundings largely cancel, so the bar
+    is relative to the whole tensor. Returns (max error / max |want|, relative L2)."""
+    g = got.astype(np.float64)
+    err = np.abs(g - want)
+    scale = np.abs(want).max()
+    rel = np.linalg.norm(g - want) / max(np.linalg.norm(want), 1e-30)
+    assert err.max() <= GRAD_MAX_REL * scale, f"{name}: max abs error {err.max():.3e} > {GRAD_MAX_REL} x {scale:.3e}"
+    assert rel <= GRAD_REL_L2, f"{name}: relative L2 error {rel:.3e} > {GRAD_REL_L2}"
+    return err.max() / max(scale, 1e-300), rel

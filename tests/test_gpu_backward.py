@@ -19,14 +19,12 @@ import pytest
 
 import gen
 import oracle
-from parity import cprob, log, oracle_select, to_dev, to_host
+from parity import cprob, grads_close, log, oracle_select, to_dev, to_host
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 P = gen.Problem
-REL_L2 = 1e-2
-MAX_REL = 1e-2
 
 CASES = {
     "gqa_ragged": (P(2, 8, 2, 4000, 128, 128, 4, 3, 4, 64, "bf16"), ("uniform_pairs", 4)),
@@ -42,16 +40,6 @@ CASES = {
     "d64_bs128_ragged": (P(1, 4, 2, 3100, 64, 128, 4, 3, 4, 64, "bf16"), ("uniform_pairs", 4)),
     "d64_bs64_group3": (P(1, 6, 2, 2500, 64, 64, 4, 2, 5, 64, "bf16"), ("uniform_pairs", 4)),
 }
-
-
-def _grads_close(name, got, want):
-    g = got.astype(np.float64)
-    err = np.abs(g - want)
-    scale = np.abs(want).max()
-    rel = np.linalg.norm(g - want) / max(np.linalg.norm(want), 1e-30)
-    assert err.max() <= MAX_REL * scale, f"{name}: max abs error {err.max():.3e} > {MAX_REL} x {scale:.3e}"
-    assert rel <= REL_L2, f"{name}: relative L2 error {rel:.3e} > {REL_L2}"
-    return err.max() / scale, rel
 
 
 def _run(p, plant, seed=17, sharp=False):
@@ -71,7 +59,7 @@ def _run(p, plant, seed=17, sharp=False):
     if p.top_k:
         assert np.array_equal(to_host(idx), oi)
     want = oracle.attend_backward(q, k, v, oi, oc, do, p.sink_len, p.block_size, p.scale)
-    res = [_grads_close(n, to_host(g), w) for n, g, w in zip(("dq", "dk", "dv"), (dq, dk, dv), want)]
+    res = [grads_close(n, to_host(g), w) for n, g, w in zip(("dq", "dk", "dv"), (dq, dk, dv), want)]
     return res
 
 

@@ -16,22 +16,12 @@ import pytest
 
 import gen
 import oracle
-from parity import (assert_outputs_close, assert_pyramid_equal, assert_selection_equal, cprob, log, split_levels,
-                    to_host)
-from test_gpu_backward import MAX_REL, REL_L2
+from parity import (assert_outputs_close, assert_pyramid_equal, assert_selection_equal, cprob, grads_close, log,
+                    split_levels, to_host)
 from test_gpu_full import _sample_units
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
-
-
-def _close(name, got, want):
-    g = got.astype(np.float64)
-    err = np.abs(g - want).max()
-    scale = np.abs(want).max()
-    rel = np.linalg.norm(g - want) / max(np.linalg.norm(want), 1e-30)
-    assert err <= MAX_REL * scale and rel <= REL_L2, f"{name}: max {err:.3e} (of {scale:.3e}), rel L2 {rel:.3e}"
-    return err / scale, rel
 
 
 @pytest.mark.timeout(900)
@@ -64,7 +54,7 @@ def test_full_backward_128k_gqa():
     for (b, g, qb) in units:
         rows = slice(qb * bs, min(p.seq_len, (qb + 1) * bs))
         heads = slice(g * G, (g + 1) * G)
-        _close(f"dq unit {(b, g, qb)}", gdq[b, heads, rows], want[0][b, heads, rows])
+        grads_close(f"dq unit {(b, g, qb)}", gdq[b, heads, rows], want[0][b, heads, rows])
     log(f"  dq of {len(units)} sampled query blocks within the bar")
     rng = np.random.default_rng(5)
     for _ in range(3):
@@ -72,8 +62,8 @@ def test_full_backward_128k_gqa():
         attending = [(0, g, qb) for qb in range(j, nb) if qb == j or j in oi[0, g, qb, :oc[0, g, qb]].tolist()]
         _, wk, wv = oracle.attend_backward(qh, kh, vh, oi, oc, doh, p.sink_len, bs, p.scale, units=attending)
         keys = slice(j * bs, (j + 1) * bs)
-        a = _close(f"dk block {(g, j)}", gdk[0, g, keys], wk[0, g, keys])
-        bb = _close(f"dv block {(g, j)}", gdv[0, g, keys], wv[0, g, keys])
+        a = grads_close(f"dk block {(g, j)}", gdk[0, g, keys], wk[0, g, keys])
+        bb = grads_close(f"dv block {(g, j)}", gdv[0, g, keys], wv[0, g, keys])
         log(f"  key block {j} of kv head {g}: {len(attending)} attending blocks; dk rel L2 {a[1]:.2e}, "
             f"dv rel L2 {bb[1]:.2e}")
 

@@ -8,8 +8,9 @@ bidirectional, mean or max summaries, bf16 or fp32. Every case runs the whole
 prefill through the C ABI -- pyramid, selection, attention -- and compares it
 with the oracle: the pyramid and the selection bit for bit, the outputs within
 the dtype's bar. Causal bf16 cases also run the fused launch, which must equal
-the two launches bit for bit; causal cases whose group size the decode takes
-also run one decode step at a drawn cache length.
+the two launches bit for bit, and the backward pass against the oracle's fp64
+gradients; causal cases whose group size the decode takes also run one decode
+step at a drawn cache length.
 """
 
 import math
@@ -19,8 +20,8 @@ import pytest
 
 import gen
 import oracle
-from parity import (assert_outputs_close, assert_pyramid_equal, assert_selection_equal, cprob, gpu_prefill, log,
-                    oracle_attend, oracle_select, to_dev, to_host)
+from parity import (assert_outputs_close, assert_pyramid_equal, assert_selection_equal, cprob, gpu_prefill,
+                    grads_close, log, oracle_attend, oracle_select, to_dev, to_host)
 
 torch = pytest.importorskip("torch")
 
@@ -89,6 +90,14 @@ def test_sweep_case(i):
         assert np.array_equal(to_host(fc), gc) and np.array_equal(to_host(fi), gi), "fused selection differs"
         assert torch.equal(fo, out) and np.array_equal(to_host(fl), lse), "fused output differs"
         log("  fused launch equals the two launches")
+        do = gen.round_to_bf16(np.random.default_rng([20261203, i, 2]).standard_normal(q.shape).astype(np.float32))
+        bout, blse, bidx, bcnt, _ = pisa.prefill(cp, qd, kd, vd, want_lse=True)
+        grads = pisa.sparse_attn_bwd(cp, qd, kd, vd, bidx, bcnt, bout, blse, to_dev(do, "bf16"))
+        torch.cuda.synchronize()
+        want = oracle.attend_backward(q, k, v, oi, oc, do, p.sink_len, p.block_size, p.scale)
+        res = [grads_close(n, to_host(g), w) for n, g, w in zip(("dq", "dk", "dv"), grads, want)]
+        log("  backward " + ", ".join(f"{n}: max {a:.2e} of max|g|, rel L2 {b:.2e}"
+                                      for n, (a, b) in zip(("dq", "dk", "dv"), res)))
 
     if p.causal and p.heads_q // p.heads_kv in (1, 2, 4, 8):
         pdec = p.replace(decode=True)
