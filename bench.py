@@ -664,8 +664,9 @@ def run_decode(args, dev):
 
     nsteps = args.decode_steps + args.warmup
     rng = np.random.default_rng(dcfg["seed"])
-    base = rng.integers(dp.seq_len // 2, dp.seq_len - nsteps, size=dp.batch)
-    lens_h = np.stack([base + s for s in range(nsteps + 1)]).astype(np.int32)
+    # lengths for two loops of nsteps steps (appended first, then beside the decode)
+    base = rng.integers(dp.seq_len // 2, dp.seq_len - 2 * nsteps, size=dp.batch)
+    lens_h = np.stack([base + s for s in range(2 * nsteps + 1)]).astype(np.int32)
     lens_d = torch.from_numpy(lens_h).to(dev)
 
     def serve(s, ev=None):
@@ -695,6 +696,25 @@ def run_decode(args, dev):
     ab = append_bytes(dp, lens_h[last].tolist(), lens_h[last + 1].tolist())
     log(f"serving step {t_srv * 1e6:.1f} us (append {t_app * 1e6:.1f} us, ragged decode {t_rdec * 1e6:.1f} us, "
         f"{rb / t_rdec / 1e9:.0f} GB/s)")
+
+    # The same loop with each step's append and decode in one call
+    # (pisa_decode_step_ragged_append): the append runs in the selection's launch.
+    def serve_one_call(s):
+        pisa.decode_step_ragged_append(dcp, dq, kc, vc, dpyr, lens_d[s], lens_d[s + 1], out=dout, idx_out=didx,
+                                       cnt_out=dcnt, workspace=ws)
+
+    for s in range(nsteps, nsteps + args.warmup):
+        serve_one_call(s)
+    torch.cuda.synchronize()
+    e0.record()
+    t0 = time.perf_counter()
+    for i in range(args.decode_steps):
+        serve_one_call(nsteps + args.warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    t_one = (time.perf_counter() - t0) / args.decode_steps
+    t_one_ev = e0.elapsed_time(e1) * 1e-3 / args.decode_steps
+    log(f"serving step in one call (append in the selection's launch) {t_one * 1e6:.1f} us")
     decode["serving"] = {
         "workload": "64 sequences at lengths uniform in [65536, 131072), one token appended per sequence per step: "
                     "pyramid append then ragged decode",
@@ -706,6 +726,13 @@ def run_decode(args, dev):
         "append_bytes": ab,
         "decode_GB/s": rb / t_rdec / 1e9,
         "decode_frac": rb / t_rdec / HBM_PEAK,
+        "one_call": {
+            "workload": "the same serving loop, each step's append and decode in one call "
+                        "(pisa_decode_step_ragged_append: the append runs in the selection's launch)",
+            "us_per_step": t_one * 1e6,
+            "us_per_step_events": t_one_ev * 1e6,
+            "tokens_per_s": dp.batch / t_one,
+        },
     }
     return decode
 

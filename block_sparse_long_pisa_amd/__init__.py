@@ -35,6 +35,7 @@ __all__ = [
     "decode_step",
     "decode_step_ragged",
     "decode_step_ragged_noalloc",
+    "decode_step_ragged_append",
     "DECODE_SCRATCH_BYTES",
     "pyramid_append",
     "prefill",
@@ -55,6 +56,7 @@ EXPORTED_SYMBOLS = [
     "pisa_decode_step",
     "pisa_decode_step_ragged",
     "pisa_decode_step_ragged_noalloc",
+    "pisa_decode_step_ragged_append",
     "pisa_pyramid_append",
     "pisa_status_string",
     "pisa_last_error",
@@ -144,6 +146,7 @@ def load_library():
         "pisa_decode_step": [P, vp, vp, vp, vp, ctypes.c_int64, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "pisa_decode_step_ragged": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "pisa_decode_step_ragged_noalloc": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
+        "pisa_decode_step_ragged_append": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp],
         "pisa_pyramid_append": [P, vp, vp, vp, vp, vp],
     }
     for name, args in sig.items():
@@ -407,6 +410,38 @@ def decode_step_ragged(p: Problem, q, k_cache, v_cache, pyramid, cache_lens, out
     _check(lib.pisa_decode_step_ragged(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pyramid),
                                        _ptr(cache_lens), _ptr(out), _ptr(lse), _ptr(idx_out), _ptr(cnt_out),
                                        _ptr(workspace), workspace.numel(), _stream(q)), "pisa_decode_step_ragged")
+    return out, lse, idx_out, cnt_out
+
+
+def decode_step_ragged_append(p: Problem, q, k_cache, v_cache, pyramid, old_lens, cache_lens, out=None, lse=None,
+                              want_lse=False, idx_out=None, cnt_out=None, want_idx=False, workspace=None):
+    """pyramid_append(p, k_cache, pyramid, old_lens, cache_lens) then decode_step_ragged at cache_lens, in the
+    launches of one decode step (the pyramid is updated in place). Returns (out, lse, idx, cnt)."""
+    torch = _torch()
+    lib = load_library()
+    dt = _tdtype(p)
+    nodes = pyramid_layout(p)[-1]
+    _expect(q, (p.batch, p.heads_q, p.head_dim), dt, "q")
+    _expect(k_cache, (p.batch, p.heads_kv, p.seq_len, p.head_dim), dt, "k_cache")
+    _expect(v_cache, (p.batch, p.heads_kv, p.seq_len, p.head_dim), dt, "v_cache")
+    _expect(pyramid, (p.batch, p.heads_kv, nodes, p.head_dim), torch.float32, "pyramid")
+    _expect(old_lens, (p.batch,), torch.int32, "old_lens")
+    _expect(cache_lens, (p.batch,), torch.int32, "cache_lens")
+    if out is None:
+        out = torch.empty_like(q)
+    _expect(out, tuple(q.shape), dt, "out")
+    if lse is None and want_lse:
+        lse = torch.empty((p.batch, p.heads_q), dtype=torch.float32, device=q.device)
+    if idx_out is None and want_idx and p.top_k:
+        idx_out = torch.empty((p.batch, p.heads_kv, p.top_k), dtype=torch.int32, device=q.device)
+    if cnt_out is None and want_idx:
+        cnt_out = torch.empty((p.batch, p.heads_kv), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, decode_workspace_size(p)), dtype=torch.uint8, device=q.device)
+    _check(lib.pisa_decode_step_ragged_append(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(pyramid),
+                                              _ptr(old_lens), _ptr(cache_lens), _ptr(out), _ptr(lse), _ptr(idx_out),
+                                              _ptr(cnt_out), _ptr(workspace), workspace.numel(), _stream(q)),
+           "pisa_decode_step_ragged_append")
     return out, lse, idx_out, cnt_out
 
 

@@ -318,6 +318,25 @@ pisa_status pisa_decode_step_ragged(const pisa_problem* p, const void* q, const 
   return e == hipSuccess ? ok() : hip_fail(e, "pisa_decode_step_ragged launch");
 }
 
+pisa_status pisa_decode_step_ragged_append(const pisa_problem* p, const void* q, const void* k_cache,
+                                           const void* v_cache, float* pyramid, const int32_t* old_lens,
+                                           const int32_t* cache_lens, void* out, float* lse, int32_t* idx_out,
+                                           int32_t* cnt_out, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  pisa::Geo g;
+  pisa_status s = make_geo(p, &g);
+  if (s != PISA_OK) return s;
+  if (g.B == 0) return ok();
+  if (old_lens == nullptr || cache_lens == nullptr) return fail(PISA_ERR_NULL, "old_lens or cache_lens is NULL");
+  if ((((uintptr_t)old_lens | (uintptr_t)cache_lens) & 3u) != 0)
+    return fail(PISA_ERR_ALIGN, "old_lens and cache_lens must be 4-byte aligned");
+  s = check_decode(g, q, k_cache, v_cache, pyramid, out, workspace, workspace_bytes);
+  if (s != PISA_OK) return s;
+  hipError_t e = pisa::launch_decode(g, q, k_cache, v_cache, pyramid, cache_lens, 0, out, lse, idx_out, cnt_out,
+                                     workspace, stream, pyramid, old_lens);
+  return e == hipSuccess ? ok() : hip_fail(e, "pisa_decode_step_ragged_append launch");
+}
+
 pisa_status pisa_decode_step_ragged_noalloc(const pisa_problem* p, const void* q, const void* k_cache,
                                             const void* v_cache, const float* pyramid, const int32_t* cache_lens,
                                             void* out, float* lse, int32_t* idx_out, int32_t* cnt_out,

@@ -17,6 +17,7 @@
 // The step is bound by HBM: it reads each attended K/V row exactly once.
 #include <mutex>
 
+#include "pisa_append.h"
 #include "pisa_internal.h"
 #include "pisa_select_common.h"
 
@@ -59,17 +60,37 @@ __device__ __forceinline__ int seq_len_of(const Geo& g, const int32_t* lens, int
   return valid ? len : 1;
 }
 
+// With old_lens given, each workgroup first appends its slab's tokens
+// [old_lens[b], lens[b]) to the pyramid (what pisa_pyramid_append does, rows
+// staged kDecAppendRows at a time in the LDS the descent uses afterwards), then
+// descends the updated pyramid: one launch fewer per serving step.
+constexpr int kDecAppendRows = 64;
+
 template <typename T, int D, int E>
 __global__ __launch_bounds__(kDecSelThreads) void decode_select_kernel(Geo g, const T* __restrict__ q,
-                                                                       const float* __restrict__ pyr,
+                                                                       const float* pyr,
                                                                        const int32_t* __restrict__ lens, int len_all,
                                                                        int32_t* __restrict__ idx,
-                                                                       int32_t* __restrict__ cnt) {
-  __shared__ BlockSmem smem;
-  __shared__ double qbar[D];
+                                                                       int32_t* __restrict__ cnt,
+                                                                       const T* __restrict__ kc, float* pyr_w,
+                                                                       const int32_t* __restrict__ old_lens) {
+  // one LDS buffer: an append's key rows, then the descent's scratch and the query mean
+  constexpr int kSmemBytes = (sizeof(BlockSmem) + 15) / 16 * 16;
+  constexpr int kSelectBytes = kSmemBytes + D * (int)sizeof(double);
+  constexpr int kAppendBytes = kAppendRowUnits<T, D, kDecAppendRows> * (int)sizeof(uint4);
+  __shared__ __attribute__((aligned(16))) unsigned char buf[kSelectBytes > kAppendBytes ? kSelectBytes : kAppendBytes];
+  BlockSmem& smem = *reinterpret_cast<BlockSmem*>(buf);
+  double* qbar = reinterpret_cast<double*>(buf + kSmemBytes);
   const int slab = blockIdx.x;
   const int b = slab / g.Hkv;
   const int kvh = slab % g.Hkv;
+  if (old_lens != nullptr) {  // uniform across the workgroup; ends with a barrier when it writes
+    uint4* rows = reinterpret_cast<uint4*>(buf);
+    if (g.pool == PISA_POOL_MAX)
+      append_slab<T, D, true, kDecSelThreads, kDecAppendRows>(g, kc, pyr_w, slab, old_lens[b], lens[b], rows);
+    else
+      append_slab<T, D, false, kDecSelThreads, kDecAppendRows>(g, kc, pyr_w, slab, old_lens[b], lens[b], rows);
+  }
   bool valid;
   const int qb = (seq_len_of(g, lens, len_all, b, valid) - 1) / g.bs;
   if (!valid) {  // uniform across the workgroup
@@ -428,7 +449,7 @@ size_t decode_workspace_bytes(const Geo& g) {
 template <typename T, int D>
 static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr,
                                   const int32_t* lens, int len_all, void* out, float* lse, int32_t* idx_out,
-                                  int32_t* cnt_out, void* wsb, hipStream_t s) {
+                                  int32_t* cnt_out, void* wsb, float* pyr_w, const int32_t* old_lens, hipStream_t s) {
   const int splits = decode_splits(g, len_all);
   DecodeWs ws = carve(g, wsb, splits);
   // the selection goes straight to the caller's buffers when they are given
@@ -440,24 +461,25 @@ static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, c
   {
     const int e = pool_slots_per_lane(g);
     const T* qt = (const T*)q;
+    const T* kt = (const T*)kc;
     if (e <= 2)
       PISA_LAUNCH(g, (decode_select_kernel<T, D, 2>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
-                         len_all, ws.idx, ws.cnt);
+                  len_all, ws.idx, ws.cnt, kt, pyr_w, old_lens);
     else if (e <= 4)
       PISA_LAUNCH(g, (decode_select_kernel<T, D, 4>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
-                         len_all, ws.idx, ws.cnt);
+                  len_all, ws.idx, ws.cnt, kt, pyr_w, old_lens);
     else if (e <= 5)  // K = 32 at fanout 8: 263 slots (the ranking's bit counts run over fewer slot groups)
       PISA_LAUNCH(g, (decode_select_kernel<T, D, 5>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
-                         len_all, ws.idx, ws.cnt);
+                  len_all, ws.idx, ws.cnt, kt, pyr_w, old_lens);
     else if (e <= 6)
       PISA_LAUNCH(g, (decode_select_kernel<T, D, 6>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
-                         len_all, ws.idx, ws.cnt);
+                  len_all, ws.idx, ws.cnt, kt, pyr_w, old_lens);
     else if (e <= 8)
       PISA_LAUNCH(g, (decode_select_kernel<T, D, 8>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
-                         len_all, ws.idx, ws.cnt);
+                  len_all, ws.idx, ws.cnt, kt, pyr_w, old_lens);
     else
       PISA_LAUNCH(g, (decode_select_kernel<T, D, 16>), dim3(slabs), dim3(kDecSelThreads), 0, s, g, qt, pyr, lens,
-                         len_all, ws.idx, ws.cnt);
+                  len_all, ws.idx, ws.cnt, kt, pyr_w, old_lens);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -479,12 +501,16 @@ static hipError_t launch_decode_d(const Geo& g, const void* q, const void* kc, c
 
 hipError_t launch_decode(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr,
                          const int32_t* lens, int cache_len, void* out, float* lse, int32_t* idx, int32_t* cnt, void* ws,
-                         hipStream_t s) {
+                         hipStream_t s, float* pyr_w, const int32_t* old_lens) {
   if (g.dtype == PISA_BF16)
-    return g.D == 128 ? launch_decode_d<uint16_t, 128>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws, s)
-                      : launch_decode_d<uint16_t, 64>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws, s);
-  return g.D == 128 ? launch_decode_d<float, 128>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws, s)
-                    : launch_decode_d<float, 64>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws, s);
+    return g.D == 128 ? launch_decode_d<uint16_t, 128>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws,
+                                                       pyr_w, old_lens, s)
+                      : launch_decode_d<uint16_t, 64>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws,
+                                                      pyr_w, old_lens, s);
+  return g.D == 128 ? launch_decode_d<float, 128>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws, pyr_w,
+                                                  old_lens, s)
+                    : launch_decode_d<float, 64>(g, q, kc, vc, pyr, lens, cache_len, out, lse, idx, cnt, ws, pyr_w,
+                                                 old_lens, s);
 }
 
 }  // namespace pisa

@@ -123,10 +123,12 @@ size_t decode_workspace_bytes(const Geo& g);
 // the allocation-free decode's workspace: a static device array per GPU
 constexpr size_t kDecodeScratchBytes = (size_t)PISA_DECODE_SCRATCH_BYTES;
 hipError_t decode_scratch_ptr(void** ptr);
-// lens: per-sequence cache lengths on the device, or nullptr for cache_len everywhere
+// lens: per-sequence cache lengths on the device, or nullptr for cache_len everywhere;
+// old_lens (device, with lens): the selection's launch also appends tokens
+// [old_lens[b], lens[b]) to the pyramid, written through pyr_w (the same pyramid)
 hipError_t launch_decode(const Geo& g, const void* q, const void* kc, const void* vc, const float* pyr,
                          const int32_t* lens, int cache_len, void* out, float* lse, int32_t* idx, int32_t* cnt, void* ws,
-                         hipStream_t s);
+                         hipStream_t s, float* pyr_w = nullptr, const int32_t* old_lens = nullptr);
 
 // pyramid update after tokens [old_lens[b], new_lens[b]) were written to the key cache
 hipError_t launch_pyramid_append(const Geo& g, const void* k, float* pyr, const int32_t* old_lens,

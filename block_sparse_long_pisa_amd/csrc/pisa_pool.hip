@@ -10,42 +10,15 @@
 // top-level node.
 #include <type_traits>
 
+#include "pisa_append.h"
 #include "pisa_internal.h"
 
 namespace pisa {
 namespace {
 
 constexpr int kPoolThreads = 256;
-constexpr int kUnroll = 8;
 constexpr int kMaxChunk = 16;  // blocks per workgroup (fanout <= 16)
 
-// Summary arithmetic: the mean (fp64 sums, one rounding) or the element-wise
-// maximum (exact).
-template <bool MX>
-struct Pool {
-  using Acc = typename std::conditional<MX, float, double>::type;
-  __device__ __forceinline__ static Acc init() { return MX ? (Acc)-__builtin_inff() : (Acc)0; }
-  __device__ __forceinline__ static Acc add(Acc a, float x) {
-    if constexpr (MX) return fmaxf(a, x);
-    else return a + (double)x;
-  }
-  // a row read from a clamped address (past the block) repeats the last row:
-  // harmless for the maximum, left out of the sum
-  __device__ __forceinline__ static Acc add_row(Acc a, float x, bool real) {
-    if constexpr (MX) return fmaxf(a, x);
-    else return a + (real ? (double)x : 0.0);
-  }
-  __device__ __forceinline__ static Acc join(Acc a, Acc b) {
-    if constexpr (MX) return fmaxf(a, b);
-    else return a + b;
-  }
-  // summary of `count` folded values; for a power-of-two count the multiply by
-  // its reciprocal is the exact quotient
-  __device__ __forceinline__ static float fin(Acc a, int count) {
-    if constexpr (MX) return a;
-    else return (float)((count & (count - 1)) == 0 ? a * (1.0 / (double)count) : a / (double)count);
-  }
-};
 
 template <typename T, int D, bool MX>
 __global__ __launch_bounds__(kPoolThreads) __attribute__((amdgpu_waves_per_eu(4))) void pool_leaf_kernel(Geo g, const T* __restrict__ k,
@@ -73,31 +46,31 @@ __global__ __launch_bounds__(kPoolThreads) __attribute__((amdgpu_waves_per_eu(4)
     typename PO::Acc acc[VEC];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc[e] = PO::init();
-    // rounds of kUnroll loads covering whole row groups run unmasked; one masked
+    // rounds of kPoolUnroll loads covering whole row groups run unmasked; one masked
     // round (clamped rows) takes the rest
-    const int nfull = (r1 - r0) / (RPI * kUnroll);  // uniform
+    const int nfull = (r1 - r0) / (RPI * kPoolUnroll);  // uniform
     const T* ptr = kb + (int64_t)(r0 + rsub) * D + col;
 #pragma unroll 1
-    for (int it = 0; it < nfull; ++it, ptr += RPI * kUnroll * D) {
-      uint4 raw[kUnroll];
+    for (int it = 0; it < nfull; ++it, ptr += RPI * kPoolUnroll * D) {
+      uint4 raw[kPoolUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) raw[u] = Wide<T>::stream(ptr + u * RPI * D);
+      for (int u = 0; u < kPoolUnroll; ++u) raw[u] = Wide<T>::stream(ptr + u * RPI * D);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kPoolUnroll; ++u) {
         float x[VEC];
         Wide<T>::widen(raw[u], x);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) acc[e] = PO::add(acc[e], x[e]);
       }
     }
-    const int r = r0 + nfull * RPI * kUnroll + rsub;
-    if (r0 + nfull * RPI * kUnroll < r1) {
-      uint4 raw[kUnroll];
+    const int r = r0 + nfull * RPI * kPoolUnroll + rsub;
+    if (r0 + nfull * RPI * kPoolUnroll < r1) {
+      uint4 raw[kPoolUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)  // unconditional loads from clamped rows, all in flight
+      for (int u = 0; u < kPoolUnroll; ++u)  // unconditional loads from clamped rows, all in flight
         raw[u] = Wide<T>::stream(kb + (int64_t)min(r + u * RPI, r1 - 1) * D + col);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kPoolUnroll; ++u) {
         // a clamped row repeats the block's last row: harmless for the maximum;
         // for the sum its bits are cleared (+0.0) before widening
         if constexpr (!MX)
@@ -147,96 +120,10 @@ __global__ __launch_bounds__(kPoolThreads) void pool_append_kernel(Geo g, const 
                                                                    float* __restrict__ pyr,
                                                                    const int32_t* __restrict__ old_lens,
                                                                    const int32_t* __restrict__ new_lens) {
-  using PO = Pool<MX>;
-  constexpr int VEC = Wide<T>::kVec;
-  constexpr int LPR = D / VEC;
-  constexpr int RPI = 64 / LPR;
+  __shared__ uint4 rows[kAppendRowUnits<T, D, 128>];  // a whole leaf at once
   const int slab = blockIdx.x;
   const int b = slab / g.Hkv;
-  const int len0 = old_lens[b];
-  const int len1 = new_lens[b];
-  if (len0 < 0 || len1 > g.N || len0 >= len1) return;  // nothing appended (uniform across the workgroup)
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int col = (lane % LPR) * VEC;
-  const int rsub = lane / LPR;
-  const T* kb = k + (int64_t)slab * g.N * D;
-  float* pb = pyr + (int64_t)slab * g.off[g.L] * D;
-  int a = len0 / g.bs, z = (len1 - 1) / g.bs;  // affected nodes of the level being built
-  // Each affected leaf: all waves copy its rows into LDS, then the first wave sums
-  // them exactly as pool_leaf_kernel sums a block -- lane slot rsub adds rows
-  // r0 + rsub, r0 + rsub + RPI, ... in ascending order, in rounds of kUnroll rows,
-  // the rows of a last partial round past r1 adding +0.0; then the slots fold by
-  // xor over the lane bits -- so the summary equals the build's bit for bit.
-  __shared__ uint4 rows[128 * D / Wide<T>::kVec];  // up to 128 rows of this lane layout's 16-byte units
-  for (int j = a; j <= z; ++j) {
-    const int r0 = j * g.bs;
-    const int r1 = min(len1, r0 + g.bs);
-    const int units = (r1 - r0) * LPR;  // 16-byte units of the leaf's rows present
-    const T* src = kb + (int64_t)r0 * D;
-    for (int e = threadIdx.x; e < units; e += kPoolThreads)
-      rows[e] = Wide<T>::raw(src + (int64_t)(e / LPR) * D + (e % LPR) * VEC);
-    __syncthreads();
-    if (wave == 0) {
-      typename PO::Acc acc[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] = PO::init();
-      const int nfull = (r1 - r0) / (RPI * kUnroll);
-      int rr = rsub;  // row within the leaf
-      for (int it = 0; it < nfull; ++it) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u, rr += RPI) {
-          float x[VEC];
-          Wide<T>::widen(rows[rr * LPR + col / VEC], x);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[e] = PO::add(acc[e], x[e]);
-        }
-      }
-      if (nfull * RPI * kUnroll < r1 - r0) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u, rr += RPI) {
-          // rows past the leaf add +0.0 to the sum (the maximum ignores them)
-          uint4 raw = rr < r1 - r0 ? rows[rr * LPR + col / VEC] : make_uint4(0u, 0u, 0u, 0u);
-          if constexpr (MX)
-            if (rr >= r1 - r0) raw = rows[(r1 - r0 - 1) * LPR + col / VEC];
-          float x[VEC];
-          Wide<T>::widen(raw, x);
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[e] = PO::add(acc[e], x[e]);
-        }
-      }
-#pragma unroll
-      for (int sh = LPR; sh < 64; sh <<= 1)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[e] = PO::join(acc[e], __shfl_xor(acc[e], sh));
-      if (rsub == 0) {
-        float outv[VEC];
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) outv[e] = PO::fin(acc[e], r1 - r0);
-        float* dst = pb + (int64_t)j * D + col;
-#pragma unroll
-        for (int e = 0; e < VEC; e += 4)
-          *reinterpret_cast<float4*>(dst + e) = make_float4(outv[e], outv[e + 1], outv[e + 2], outv[e + 3]);
-      }
-    }
-    __syncthreads();
-  }
-  int present = z + 1;  // nodes of the level below that hold tokens before len1
-  for (int l = 1; l < g.L; ++l) {
-    const int na = a / g.f, nz = z / g.f;
-    for (int e = threadIdx.x; e < (nz - na + 1) * D; e += kPoolThreads) {
-      const int n = na + e / D, c = e % D;
-      const int c0 = n * g.f;
-      const int c1 = min(c0 + g.f, present);
-      typename PO::Acc sum = PO::init();
-      for (int ch = c0; ch < c1; ++ch) sum = PO::add(sum, pb[(int64_t)(g.off[l - 1] + ch) * D + c]);
-      pb[(int64_t)(g.off[l] + n) * D + c] = PO::fin(sum, c1 - c0);
-    }
-    __syncthreads();
-    a = na;
-    z = nz;
-    present = (present + g.f - 1) / g.f;
-  }
+  append_slab<T, D, MX, kPoolThreads, 128>(g, k, pyr, slab, old_lens[b], new_lens[b], rows);
 }
 
 // Levels lo..top (lo >= 2) in one launch: a workgroup owns one node of level

@@ -229,6 +229,30 @@ pisa_status pisa_decode_step_ragged(const pisa_problem* p, const void* q, const 
                                     int32_t* idx_out, int32_t* cnt_out, void* workspace, size_t workspace_bytes,
                                     hipStream_t stream);
 
+/* A serving step in the launches of one decode: the pyramid append of each
+ * sequence's new tokens and the ragged decode at the new lengths (the PISA page,
+ * "Le pooling comme première réduction": only the nodes holding new keys change;
+ * the Pulsar page, "Phase 2 : Encodage de la requête globale": the split partial
+ * attentions merged). Computes, bit for bit, what pisa_pyramid_append(p, k_cache,
+ * pyramid, old_lens, cache_lens) followed by pisa_decode_step_ragged(p, q, ...,
+ * cache_lens, ...) compute, for any lengths:
+ *   pyramid: as for pisa_pyramid_append (updated in place) and then read as for
+ *            pisa_decode_step_ragged;
+ *   old_lens: device int32 [batch], the lengths the pyramid is up to date for;
+ *   cache_lens: device int32 [batch], the new lengths (tokens [old_lens[b],
+ *               cache_lens[b]) already in the caches), at which the step decodes;
+ *   all other arguments as for pisa_decode_step_ragged.
+ * The workgroup that selects for a (batch, kv head) first appends its tokens,
+ * then descends the updated pyramid, so the step takes the decode's three
+ * launches instead of four. Lengths are handled as by the two calls: a sequence
+ * whose append would be skipped is not appended, and one whose cache_lens[b]
+ * lies outside [1, seq_len] attends nothing. */
+pisa_status pisa_decode_step_ragged_append(const pisa_problem* p, const void* q, const void* k_cache,
+                                           const void* v_cache, float* pyramid, const int32_t* old_lens,
+                                           const int32_t* cache_lens, void* out, float* lse, int32_t* idx_out,
+                                           int32_t* cnt_out, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream);
+
 /* Largest decode workspace the allocation-free entry point can serve: 16 MiB
  * (workload of 64 sequences x 8 KV heads x 4 query heads per KV head, d = 128,
  * K = 32 needs about 6.5 MiB). */

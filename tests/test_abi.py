@@ -179,6 +179,18 @@ def test_ragged_decode_and_append_validation(lib):
     assert append(prob=_p(seq_len=0)) == OK
     assert lib.pisa_pyramid_append(None, fake, fake, fake, fake, None) == ENULL
 
+    def both(old=fake, lens=fake, pyr=fake, ws_bytes=n.value, prob=p):
+        return lib.pisa_decode_step_ragged_append(ctypes.byref(prob), fake, fake, fake, pyr, old, lens, fake, None,
+                                                  None, None, ws, ws_bytes, None)
+
+    assert both(old=None) == ENULL
+    assert both(lens=None) == ENULL
+    assert both(pyr=None) == ENULL
+    assert both(old=ctypes.c_void_p(4098)) == EALIGN
+    assert both(ws_bytes=n.value - 1) == EWS
+    assert both(prob=_p(seq_len=4096, heads_q=6, heads_kv=2)) == EUNSUP
+    assert both(prob=_p(batch=0)) == OK
+
 
 def test_backward_validation(lib):
     p = _p(seq_len=4096)

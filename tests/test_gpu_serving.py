@@ -10,7 +10,9 @@ cache lengths, and the pyramid kept up to date as tokens are appended.
 * a short serving loop (append the new token, update the pyramid, decode) checked
   step by step against the oracle;
 * the append of a step run before, after and beside that step's decode: the same
-  results bit for bit.
+  results bit for bit;
+* the append and the decode in one call (pisa_decode_step_ragged_append) against
+  the two calls, bit for bit.
 """
 
 import math
@@ -115,6 +117,10 @@ APPEND = {
     "f32_d64_fanout2_deep": (P(4, 2, 1, 1500, 64, 32, 2, 5, 3, 32, "f32"),
                              [31, 0, 700, 1499], [32, 1500, 701, 1499]),
     "bf16_one_level": (P(2, 2, 2, 1024, 128, 128, 4, 1, 2, 64, "bf16"), [100, 1000], [101, 1024]),
+    # one leaf deep in a fanout-16 tree: 15 complete siblings at each of its three
+    # coarser levels, and a leaf just past a level-2 node boundary
+    "bf16_fanout16_many_siblings": (P(2, 1, 1, 131072, 128, 32, 16, 4, 4, 64, "bf16"), [131070, 4096],
+                                    [131071, 4097]),
 }
 
 
@@ -250,6 +256,59 @@ def test_append_may_run_beside_the_decode_of_its_step():
         for x, y, z in zip(a[s], b[s], c[s]):
             assert np.array_equal(x, y) and np.array_equal(x, z), f"step {s}"
     log(f"  lengths {lens[0]} -> {lens[-1]}: three orders identical, counts {a[-1][3].reshape(-1).tolist()}")
+
+
+ONE_CALL = {
+    "gqa4_bs64_mean": P(4, 8, 2, 1200, 128, 64, 4, 3, 4, 64, "bf16", decode=True),
+    "gqa4_bs64_max": P(4, 8, 2, 1200, 128, 64, 4, 3, 4, 64, "bf16", decode=True, pool="max"),
+    "fp32_group1_bs32": P(4, 2, 2, 700, 64, 32, 4, 3, 3, 40, "f32", decode=True),
+    "group8_bs128": P(2, 16, 2, 2048, 128, 128, 8, 2, 6, 64, "bf16", decode=True),
+}
+
+
+@pytest.mark.parametrize("name", list(ONE_CALL))
+def test_append_and_decode_in_one_call_match_the_two_calls(name):
+    """pisa_decode_step_ragged_append against pisa_pyramid_append followed by
+    pisa_decode_step_ragged: outputs, lse, selections and the whole pyramid equal
+    bit for bit after every step. The steps append one token (the append beside
+    the descent), several tokens across a block boundary (the selecting workgroup
+    appends first), nothing (equal lengths), and a length past the capacity
+    (nothing appended, nothing attended)."""
+    import block_sparse_long_pisa_amd as pisa
+
+    p = ONE_CALL[name]
+    log(f"one-call append + decode {name}: {p}")
+    cap, bs = p.seq_len, p.block_size
+    q, k, v, _ = gen.host_decode_inputs(p, 71, _scale(p), cap)
+    cp = cprob(p)
+    kd, vd = to_dev(k, p.dtype), to_dev(v, p.dtype)
+    start = [bs - 2, 2 * bs - 1, cap // 2, cap - 6][:p.batch] + [bs + 3] * max(0, p.batch - 4)
+    deltas = [[1] * p.batch, [3] * p.batch, [1, 0, 1, 2][:p.batch] + [1] * max(0, p.batch - 4),
+              [1] * (p.batch - 1) + [7], [bs + 1] * (p.batch - 1) + [0]]
+    lens = [start]
+    for d in deltas:
+        lens.append([n + x for n, x in zip(lens[-1], d)])
+    lens_d = [torch.tensor(l, dtype=torch.int32, device="cuda") for l in lens]
+    rng = np.random.default_rng(6)
+    tdt = torch.bfloat16 if p.dtype == "bf16" else torch.float32
+    qs = [torch.from_numpy(gen.round_to_bf16((rng.standard_normal((p.batch, p.heads_q, p.head_dim)) *
+                                              _scale(p)).astype(np.float32))).to(tdt).cuda() for _ in deltas]
+    pyr_a = pisa.build_pyramid(cp, kd)  # the whole capacity: the nodes a decode reads are exact
+    pyr_b = pyr_a.clone()
+    ws = torch.empty(max(1, pisa.decode_workspace_size(cp)), dtype=torch.uint8, device="cuda")
+    for s in range(len(deltas)):
+        pisa.pyramid_append(cp, kd, pyr_a, lens_d[s], lens_d[s + 1])
+        ra = pisa.decode_step_ragged(cp, qs[s], kd, vd, pyr_a, lens_d[s + 1], want_lse=True, want_idx=True,
+                                     workspace=ws)
+        ra = [to_host(x).copy() for x in ra]
+        rb = pisa.decode_step_ragged_append(cp, qs[s], kd, vd, pyr_b, lens_d[s], lens_d[s + 1], want_lse=True,
+                                            want_idx=True, workspace=ws)
+        rb = [to_host(x).copy() for x in rb]
+        torch.cuda.synchronize()
+        for n, x, y in zip(("out", "lse", "idx", "cnt"), ra, rb):
+            assert np.array_equal(x, y), f"step {s}: {n} differs"
+        assert torch.equal(pyr_a, pyr_b), f"step {s}: pyramid differs"
+    log(f"  lengths {lens[0]} -> {lens[-1]}: one call equals two, step by step")
 
 
 def test_append_matches_the_build_bit_for_bit_on_keys_spanning_many_binades():
