@@ -58,10 +58,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2
   // of its XCD x, one slab after another, so that an XCD's L2 holds the keys and
   // values of one slab at a time. order 1: all of one slab's items before the
   // next slab's, over the whole GPU. order 0: consecutive items walk the slabs.
+  // order 3: as order 0, but the parts of a unit go to workgroups of one XCD
+  // (i, i + 8, ...), so that the parts after the first find its tiles in that
+  // XCD's L2 (the grid is a multiple of 8 * parts).
   const int slabs = g.B * g.Hkv;
   const int64_t items = (int64_t)g.nb * slabs * parts;
   const int64_t per_slab = (int64_t)g.nb * parts;
-  const int64_t first = order == 2 ? blockIdx.x / 8 : blockIdx.x;
+  const int64_t first = order == 2   ? blockIdx.x / 8
+                        : order == 3 ? ((int64_t)(blockIdx.x / 8) / parts * 8 + blockIdx.x % 8) * parts +
+                                           (blockIdx.x / 8) % parts
+                                     : blockIdx.x;
   const int64_t stride = order == 2 ? gridDim.x / 8 : gridDim.x;
   const int64_t count = order == 2 ? items / 8 : items;
   for (int64_t wg = first; wg < count; wg += stride) {
@@ -74,6 +80,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW <= 2
       slab = (int)(wg / per_slab);
       part = (int)(wg % parts);
       qb = g.nb - 1 - (int)((wg % per_slab) / parts);
+    } else if (order == 3) {
+      const int64_t unit_i = wg / parts;
+      part = (int)(wg % parts);
+      slab = (int)(unit_i % slabs);
+      qb = g.nb - 1 - (int)(unit_i / slabs);
     } else {
       slab = (int)(wg % slabs);
       part = (int)((wg / slabs) % parts);
@@ -176,9 +187,13 @@ hipError_t launch_bf16(const Geo& g, const void* q, const void* k, const void* v
   const int64_t grid = std::min<int64_t>(items, (int64_t)kAttnWgPerCu * cus);
   // item order: slabs divisible among the 8 XCDs -- each XCD walks its own
   // slabs, one after another (2); otherwise many slabs -- one slab after another
-  // over the whole GPU (1); few -- slab-fastest (0)
+  // over the whole GPU (1); few -- slab-fastest, with a unit's parts on one XCD
+  // when the grid allows it (3), else as they come (0)
   const int slabs = g.B * g.Hkv;
-  const int order = slabs % 8 == 0 && grid % 8 == 0 ? 2 : slabs > 8 ? 1 : 0;
+  const int order = slabs % 8 == 0 && grid % 8 == 0 ? 2
+                    : slabs > 8                       ? 1
+                    : parts > 1 && grid % (8 * parts) == 0 ? 3
+                                                           : 0;
   PISA_LAUNCH(g, (attn_bf16_kernel<D, BS, NW>), dim3((unsigned)grid), dim3(NW * 64), 0, s, g,
                      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, idx, cnt, (uint16_t*)out, lse, parts,
                      order);
