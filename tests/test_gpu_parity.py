@@ -70,6 +70,28 @@ def test_prefill_parity(name):
     log(f"  max abs err {err:.2e}")
 
 
+def test_parts_of_a_unit_on_one_xcd_with_a_partial_last_round():
+    """Two slabs and two parts per unit (GQA 16q/2kv, blocks of 64: eight-wave
+    units of 256 of the 512 rows) over 600 query blocks: 2400 (unit, part) items
+    on the persistent grid of 2048 workgroups, so the attention takes the order
+    that keeps a unit's parts on one XCD, with a second, partial round. The
+    outputs of query blocks from both rounds (the heaviest units run first) are
+    compared with the oracle; every selection is compared."""
+    p = P(1, 16, 2, 600 * 64 - 21, 128, 64, 4, 3, 4, 64, "bf16")
+    log(f"case parts on one XCD: {p}")
+    q, k, v, _ = _inputs(p, ("uniform_pairs", 4), None, seed=29)
+    levels, gi, gc, out, lse = gpu_prefill(p, to_dev(q, p.dtype), to_dev(k, p.dtype), to_dev(v, p.dtype))
+    pyr, oi, oc = oracle_select(p, q, k)
+    assert_pyramid_equal(levels, pyr)
+    assert_selection_equal(gi, gc, oi, oc)
+    nb = p.n_blocks
+    qbs = sorted(set(list(range(0, 96, 5)) + list(range(nb - 520, nb, 23)) + [nb - 1]))
+    units = [(0, g, qb) for g in range(p.heads_kv) for qb in qbs]
+    o, ol = oracle.attend(q, k, v, oi, oc, p.sink_len, p.block_size, p.scale, blocks=units)
+    err = assert_outputs_close(p, to_host(out), o, lse, ol)
+    log(f"  {len(units)} units: max abs err {err:.2e}")
+
+
 # every (head dim, block, waves per unit) the bf16 attention is built for: the
 # library takes 8 waves when the unit's (head, 32-row) pairs G*bs/32 are a
 # multiple of 8, else 4, 2 or 1, so G = NW*32/bs picks each one
