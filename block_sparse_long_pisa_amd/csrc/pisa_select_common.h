@@ -146,6 +146,12 @@ __device__ __forceinline__ int slot_node(int p, int nchild, int f, const int* ke
   return p < nchild ? kept[p / f] * f + p % f : anc_first + (p - nchild);
 }
 
+// Node rows are scored by 16-lane groups: lane s of a group holds the 16-byte
+// units s, s + 16, ... of the row (four floats each), so that each load
+// instruction reads whole 128-byte lines of its four rows. qcol(s, e) is the
+// column of the e-th value lane s holds.
+__device__ __forceinline__ int qcol(int s, int e) { return ((e >> 2) * 16 + s) * 4 + (e & 3); }
+
 // Score pool slots [0, M) into sm.sc (fp64 dot products with the query mean);
 // the slots' nodes come from sm.node (-1: no node; its score is meaningless).
 // 16 lanes per node, four nodes per wave load, U loads in flight.
@@ -163,9 +169,9 @@ __device__ __forceinline__ void score_slots(const float* __restrict__ lvl, int M
       // slots without a node read node 0 (always present) so that no load is
       // conditional; their scores are never ranked
       const int n = max(sm.node[base + u * 4 + grp], 0);
-      const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)n * D + sub * DPL);
+      const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)n * D);
 #pragma unroll
-      for (int e4 = 0; e4 < DPL / 4; ++e4) x[u][e4] = row[e4];
+      for (int e4 = 0; e4 < DPL / 4; ++e4) x[u][e4] = row[e4 * 16 + sub];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -197,7 +203,7 @@ __device__ void wave_descend(const Geo& g, const float* __restrict__ ps, int qb,
   }
   double qv[DPL];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) qv[e] = sm.qbar[(lane & 15) * DPL + e];
+  for (int e = 0; e < DPL; ++e) qv[e] = sm.qbar[qcol(lane & 15, e)];
   const int L = g.L;
   // top level: causal -- the complete nodes before the ancestor that hold a
   // non-sink block; bidirectional -- every node holding a candidate
@@ -299,7 +305,7 @@ __device__ void block_descend(const Geo& g, const float* __restrict__ ps, int qb
   }
   double qv[DPL];
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) qv[e] = qbar[sub * DPL + e];
+  for (int e = 0; e < DPL; ++e) qv[e] = qbar[qcol(sub, e)];
   const int L = g.L;
   int lo = g.j0 / g.span[L - 1];
   int M = max(0, qb / g.span[L - 1] - lo);
@@ -334,10 +340,9 @@ __device__ void block_descend(const Geo& g, const float* __restrict__ ps, int qb
         for (int u = 0; u < U; ++u) {
           const int p = base + u * NG + grp;
           const int n = p < M ? sm.id[p] : INT_MAX;
-          const float4* row =
-              reinterpret_cast<const float4*>(lvl + (int64_t)(n != INT_MAX ? n : stand_in) * D + sub * DPL);
+          const float4* row = reinterpret_cast<const float4*>(lvl + (int64_t)(n != INT_MAX ? n : stand_in) * D);
 #pragma unroll
-          for (int e4 = 0; e4 < DPL / 4; ++e4) x[u][e4] = row[e4];
+          for (int e4 = 0; e4 < DPL / 4; ++e4) x[u][e4] = row[e4 * 16 + sub];
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
