@@ -173,7 +173,11 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(Geo g, const float* __res
   }
 }
 
-constexpr int kAttnWgPerCu = 8;  // persistent workgroups per compute unit
+// persistent workgroups per compute unit: units of at most two waves take as
+// many as fit at once (four, one stage of LDS each), so that an XCD visits each
+// of its slabs once; the eight-wave units take eight (one resident at a time)
+template <int NW>
+constexpr int kAttnWgPerCu = NW <= 2 ? 4 : 8;
 
 template <int D, int BS, int NW>
 hipError_t launch_bf16(const Geo& g, const void* q, const void* k, const void* v, const int32_t* idx,
@@ -184,7 +188,7 @@ hipError_t launch_bf16(const Geo& g, const void* q, const void* k, const void* v
   int cus = 0;
   hipError_t e = device_cus(&cus);
   if (e != hipSuccess) return e;
-  const int64_t grid = std::min<int64_t>(items, (int64_t)kAttnWgPerCu * cus);
+  const int64_t grid = std::min<int64_t>(items, (int64_t)kAttnWgPerCu<NW> * cus);
   // item order: slabs divisible among the 8 XCDs -- each XCD walks its own
   // slabs, one after another (2); otherwise many slabs -- one slab after another
   // over the whole GPU (1); few -- slab-fastest, with a unit's parts on one XCD
