@@ -30,32 +30,32 @@ BF16_PEAK = 2.5e15  # flop/s, dense bf16 matrix cores
 # "w2/..." and "w5/...", on the 32K and 1M prefills), from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch). Each counter is scaled by what
 # it reads for a plain device copy of 1 GiB into 1 GiB: FETCH_SIZE reports
-# 524339.3 KiB for the copy's 1 GiB of reads, WRITE_SIZE 1048576 KiB for its
+# 524337.5 KiB for the copy's 1 GiB of reads, WRITE_SIZE 1048576 KiB for its
 # writes. A figure holds only for the kernel source it was taken on: the sources
 # are hashed at run time and a changed kernel reports null.
-COPY_SCALE = {"fetch": 1048576.0 / 524339.25, "write": 1048576.0 / 1048576.0}
+COPY_SCALE = {"fetch": 1048576.0 / 524337.5, "write": 1048576.0 / 1048576.0}
 MEASURED_TRAFFIC = {
     # step: (sources, sha256 prefix of their bytes in this order, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    "attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "8e34ee75f52102f2",
-                  5859511.4, 1048577.3),
+    "attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "661f4e2286e61980",
+                  5855513.3, 1048576.9),
     "pyramid": (("pisa_pool.hip", "pisa_internal.h"), "3bf04d0514e54278",
-                131123.5 + 275.7, 4608.1 + 72.0),  # leaf and level 1, then levels 2 and up
-    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "61caf531439166e2",
-               526688.2, 1056.0),
+                131123.5 + 275.7, 4608.2 + 72.0),  # leaf and level 1, then levels 2 and up
+    "select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "e9aeb64bfaa4b868",
+               526688.7, 1056.0),
     # select + split attention + merge of the plain decode step (its first four dispatches of each)
-    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h", "pisa_append.h"), "1b12fd772584ebc6",
-               50295.7 + 550545.3 + 3601.3, 80.0 + 6336.0 + 512.0),
+    "decode": (("pisa_decode.hip", "pisa_select_common.h", "pisa_internal.h", "pisa_append.h"), "d8dca548eff013a9",
+               50290.3 + 550539.7 + 3601.3, 80.0 + 6336.0 + 512.0),
     # the 32K MHA (w2) and 1M one-group (w5) prefills, from the same runs
-    "w2/attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "8e34ee75f52102f2",
-                     2679770.4, 263464.3),
-    "w2/pyramid": (("pisa_pool.hip", "pisa_internal.h"), "3bf04d0514e54278", 131123.3 + 531.7, 9216.0 + 128.0),
-    "w2/select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "61caf531439166e2",
-                  135745.4, 1089.3),
-    "w5/attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "8e34ee75f52102f2",
-                     15643406.7, 1049232.6),
-    "w5/pyramid": (("pisa_pool.hip", "pisa_internal.h"), "3bf04d0514e54278", 131123.4 + 8.9 + 275.7, 4608.2 + 1.0 + 72.0),
-    "w5/select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "61caf531439166e2",
-                  543240.4, 2125.6),
+    "w2/attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "661f4e2286e61980",
+                     2448433.1, 263290.1),
+    "w2/pyramid": (("pisa_pool.hip", "pisa_internal.h"), "3bf04d0514e54278", 131123.2 + 531.7, 9216.0 + 128.0),
+    "w2/select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "e9aeb64bfaa4b868",
+                  135745.9, 1088.5),
+    "w5/attention": (("pisa_attn.hip", "pisa_attn_fwd.h", "pisa_attn_common.h", "pisa_internal.h"), "661f4e2286e61980",
+                     15704745.0, 1049570.2),
+    "w5/pyramid": (("pisa_pool.hip", "pisa_internal.h"), "3bf04d0514e54278", 131123.9 + 8.9 + 275.7, 4608.2 + 1.0 + 72.0),
+    "w5/select": (("pisa_select.hip", "pisa_select_common.h", "pisa_internal.h"), "e9aeb64bfaa4b868",
+                  543207.3, 2125.9),
 }
 
 
